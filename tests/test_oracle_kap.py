@@ -1,0 +1,167 @@
+"""Pins for the Kernel-Aware Proxy oracle (CPU, float64).
+
+* hand-derived golden cases (tests/golden/kap_worked_examples.json) for the
+  flag-grouped order, HRM-first truncation and tie-breaks (CoSA (paperpeel)
+  App. C.1 and §4.2 "Flag-grouped sorting");
+* the pooled-score identity: the pooled logit equals the mean of the exact
+  logits over the (proxy row x key block) sub-block, by brute force;
+* the structural invariants of M_KAP the pages state: a subset of the causal
+  candidates, HRM group before the non-HRM group, each group sorted by score,
+  length equal to the budget count (§4.1, App. C.1);
+* budget 100% keeps every candidate.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import cosa_inputs as ci
+from oracle import kap
+from oracle.paging import materialise
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "kap_worked_examples.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _example_arrays(ex):
+    L, g, kb, D = ex["L"], ex["rows_per_proxy"], ex["kv_block"], ex["D"]
+    q = np.zeros((L, D))
+    for r, vec in enumerate(ex["proxy_row_query"]):
+        q[r * g:(r + 1) * g] = vec
+    k = np.zeros((L, D))
+    for j, vec in enumerate(ex["block_key"]):
+        k[j * kb:(j + 1) * kb] = vec
+    return q, k
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_golden_worked_example(idx):
+    ex = _golden()["examples"][idx]
+    q, k = _example_arrays(ex)
+    res = kap.head_tiles(q, k, ex["scale"], ex["q_block"], ex["kv_block"],
+                         kap.budget_ppm(ex["budget"]), ex["rows_per_proxy"])
+    assert list(res) == [0]
+    t = res[0]
+    assert t.n == ex["expect_n"]
+    assert np.allclose(t.w, ex["expect_w"], rtol=0, atol=1e-15)
+    assert list(t.hrm) == ex["expect_hrm"]
+    assert list(t.order) == ex["expect_order"]
+    assert t.k == ex["expect_k"]
+    assert list(t.blocks) == ex["expect_blocks"]
+    assert t.hrm_count == ex["expect_hrm_count"]
+
+
+def test_budget_counts_hand_values():
+    for n, beta, want in _golden()["budget_counts"]["cases"]:
+        assert kap.budget_count(n, kap.budget_ppm(beta)) == want, (n, beta)
+    assert kap.budget_count(0, 100000) == 0
+    with pytest.raises(ValueError):
+        kap.budget_ppm(0.0)
+    with pytest.raises(ValueError):
+        kap.budget_ppm(1.5)
+
+
+def test_pooled_score_equals_mean_of_exact_logits():
+    rng = np.random.default_rng(3)
+    L, D, qb, kb, g = 77, 5, 32, 8, 16
+    q, k = rng.standard_normal((L, D)), rng.standard_normal((L, D))
+    scale = 0.37
+    kbar = kap.pooled_keys(k, kb)
+    qbar, last, valid = kap.pooled_queries(q, qb, g)
+    for i in range(qbar.shape[0]):
+        for r in range(qbar.shape[1]):
+            rows = [t for t in range(i * qb + r * g, i * qb + (r + 1) * g) if t < L]
+            assert valid[i, r] == bool(rows)
+            if not rows:
+                continue
+            assert last[i, r] == rows[-1]
+            for j in range(kbar.shape[0]):
+                keys = [u for u in range(j * kb, (j + 1) * kb) if u < L]
+                brute = sum(scale * float(q[a] @ k[u]) for a in rows for u in keys)
+                brute /= len(rows) * len(keys)
+                assert abs(scale * float(qbar[i, r] @ kbar[j]) - brute) < 1e-13
+
+
+def _check_tile_invariants(t: kap.TileProxy, last_rows, kv_block):
+    n = t.n
+    assert n == int(max(last_rows)) // kv_block + 1
+    order = list(t.order)
+    assert sorted(order) == list(range(n))                    # a permutation
+    blocks = list(t.blocks)
+    assert len(blocks) == t.k and len(set(blocks)) == len(blocks)
+    flags = [bool(t.hrm[j]) for j in order]
+    # every HRM block precedes every non-HRM block
+    assert flags == sorted(flags, reverse=True)
+    # each group sorted by w desc, then block index asc
+    for a, b in zip(order, order[1:]):
+        if t.hrm[a] == t.hrm[b]:
+            assert (t.w[a] > t.w[b]) or (t.w[a] == t.w[b] and a < b)
+    # HRM flags: exactly the arg-max blocks of the proxy rows
+    am = set(int(np.argmax(row)) for row in t.scores)
+    assert set(np.flatnonzero(t.hrm).tolist()) == am
+    # probabilities: each proxy row sums to 1 over its candidates only
+    for r, lr in enumerate(last_rows):
+        c = int(lr) // kv_block + 1
+        assert abs(t.probs[r, :c].sum() - 1) < 1e-12
+        assert np.all(t.probs[r, c:] == 0)
+    assert abs(t.w.sum() - 1) < 1e-12
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_skip"])
+def test_tiny_mask_invariants(name):
+    w = ci.get(name)
+    x = ci.make(w).bf16_rounded()
+    m = kap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
+                               w.q_block, w.page_size, w.budget, w.softmax_scale)
+    L = w.seqlens[0]
+    nqb = (L + w.q_block - 1) // w.q_block
+    assert m.capacity == kap.budget_count((L + 63) // 64, kap.budget_ppm(w.budget))
+    for h in range(w.num_q_heads):
+        for i in range(nqb):
+            t = m.tiles[(0, h, i)]
+            last_rows = [min(i * w.q_block + (r + 1) * 16, L) - 1
+                         for r in range(w.q_block // 16) if i * w.q_block + r * 16 < L]
+            _check_tile_invariants(t, last_rows, w.page_size)
+            cnt = m.counts[0, h, i]
+            assert cnt == kap.budget_count(i + 1, kap.budget_ppm(w.budget))
+            assert np.array_equal(m.blocks[0, h, i, :cnt], t.blocks)
+            assert np.all(m.blocks[0, h, i, cnt:] == -1)
+            assert np.array_equal(m.pages[0, h, i, :cnt], x.page_table[0][t.blocks])
+            assert m.hrm_counts[0, h, i] == t.hrm_count
+
+
+def test_budget_full_selects_every_candidate_ragged_batch():
+    w = ci.get("tiny").with_(seqlens=(200, 64, 1, 130), num_q_heads=4, num_kv_heads=2,
+                              shuffled_pages=True, spare_pages=3)
+    x = ci.make(w).bf16_rounded()
+    m = kap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, 2, 64, 64,
+                               1.0, w.softmax_scale)
+    for b, L in enumerate(w.seqlens):
+        for h in range(4):
+            for i in range((L + 63) // 64):
+                n = (min((i + 1) * 64, L) - 1) // 64 + 1
+                assert m.counts[b, h, i] == n
+                assert sorted(m.blocks[b, h, i, :n].tolist()) == list(range(n))
+            assert np.all(m.counts[b, h, (L + 63) // 64:] == 0)
+
+
+def test_kap_independent_of_page_placement():
+    # the same logical keys stored under two different page permutations give
+    # the same mask, and pages follow each table
+    w = ci.get("tiny").with_(seqlens=(300,), shuffled_pages=False, spare_pages=0)
+    x = ci.make(w).bf16_rounded()
+    perm = np.array([3, 0, 4, 1, 2])
+    kp = np.empty_like(x.k_pool)
+    kp[perm] = x.k_pool[x.page_table[0, :5]]
+    pt = perm[None, :].astype(np.int32)
+    a = kap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, 2, 64, 64, 0.5, 0.125)
+    b = kap.proxy_ordered_mask(x.q, kp, pt, x.cu_seqlens, 2, 64, 64, 0.5, 0.125)
+    assert np.array_equal(a.blocks, b.blocks)
+    assert np.array_equal(b.pages[b.blocks >= 0], perm[b.blocks[b.blocks >= 0]])
+    assert np.allclose(materialise(kp, pt[0], 300, 64), materialise(x.k_pool, x.page_table[0], 300, 64))
