@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark: CoSA prefill attention (KAP ordered mask + OSK) at 128K on one GPU.
+
+One step = one layer's sparse prefill on resident inputs: the proxy ordered
+mask (cosa_proxy_ordered_mask) followed by the ordered-skipping prefill
+(cosa_osk_prefill).  The dense causal kernel (cosa_dense_prefill) on the same
+inputs is timed separately as the speedup baseline.  Inputs are seeded
+synthetic tensors with the Llama-3.1-8B attention shape (32 query / 8 KV
+heads, head_dim 128, 131072 tokens, query tile 128, KV page 64, shuffled page
+table, planted sink / band / stripe structure).
+
+Prints one JSON line (rank 0).  Times are HIP-event times on the stream the
+kernels run on; ``roofline`` describes the dominant kernel (the OSK);
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same layer
+and extrapolates to the whole layer.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama128k")
+    ap.add_argument("--budget", type=float, default=None)
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tiles", type=int, default=24,
+                    help="oracle sample size (tiles) for the CPU baseline")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the workload's budget x tau sweep (extra JSON lines)")
+    ap.add_argument("--only", choices=["all", "kap", "osk", "dense"], default="all",
+                    help="launch only one kernel kind (for profiler runs)")
+    return ap.parse_args()
+
+
+def flops_per_slot(q_block: int, head_dim: int, page: int) -> float:
+    return 2.0 * q_block * page * head_dim
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by KV head with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_sparse_long_kap_amd as bk
+    import cosa_inputs as ci
+    from block_sparse_long_kap_amd import _lib
+
+    _lib.load()
+    w = ci.get(args.workload)
+    budget = w.budget if args.budget is None else args.budget
+    tau = w.tau if args.tau is None else args.tau
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    x = ci.make(w)
+    gen_s = time.time() - t0
+    q = torch.from_numpy(x.q).to(torch.bfloat16).to(dev)
+    kp = torch.from_numpy(x.k_pool).to(torch.bfloat16).to(dev)
+    vp = torch.from_numpy(x.v_pool).to(torch.bfloat16).to(dev)
+    prob = bk.Problem(cu_seqlens=torch.from_numpy(x.cu_seqlens).to(dev),
+                      page_table=torch.from_numpy(x.page_table).to(dev),
+                      num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                      head_dim=w.head_dim, max_seqlen=w.max_seqlen, total_q=w.total_tokens,
+                      num_pages=x.k_pool.shape[0], q_block=w.q_block, page_size=w.page_size,
+                      softmax_scale=w.softmax_scale)
+    ws = bk.KapWorkspace(prob)
+    mask = bk.proxy_ordered_mask(prob, q, kp, budget, workspace=ws)
+    rec = bk.osk_prefill(prob, q, kp, vp, mask, tau, record=True)
+    out = bk.PrefillOutput(out=torch.empty_like(q), lse=torch.empty_like(rec.lse))
+    dout = bk.PrefillOutput(out=torch.empty_like(q), lse=torch.empty_like(rec.lse))
+    torch.cuda.synchronize()
+    stats = rec.row_stats.cpu().numpy().reshape(-1, 2)
+    visited = int(stats[:, 0].sum())
+    skipped = int(stats[:, 1].sum())
+    computed = visited - skipped
+    fps = flops_per_slot(w.q_block, w.head_dim, w.page_size)
+    osk_flops = fps * (visited + computed)
+    lens = np.diff(x.cu_seqlens)
+    causal_slots = 0
+    for L in lens:
+        for i in range((int(L) + w.q_block - 1) // w.q_block):
+            causal_slots += (min((i + 1) * w.q_block, int(L)) - 1) // w.page_size + 1
+    causal_slots *= w.num_q_heads
+    dense_flops = 2 * fps * causal_slots
+
+    stream = torch.cuda.current_stream(dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(times):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        if args.only in ("all", "kap"):
+            bk.proxy_ordered_mask(prob, q, kp, budget, workspace=ws, out=mask)
+        e1.record(stream)
+        if args.only in ("all", "osk"):
+            bk.osk_prefill(prob, q, kp, vp, mask, tau, out=out)
+        e2.record(stream)
+        times.append((e0, e1, e2))
+
+    for _ in range(args.warmup):
+        step([])
+    torch.cuda.synchronize()
+    times = []
+    s0, s1 = ev(), ev()
+    s0.record(stream)
+    t_wall = time.perf_counter()
+    for _ in range(args.steps):
+        step(times)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    ms_step = s0.elapsed_time(s1) / args.steps
+    kap_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in times]))
+    osk_ms = float(np.mean([b.elapsed_time(c) for _, b, c in times]))
+
+    dense_ms = None
+    if not args.no_dense and args.only in ("all", "dense"):
+        for _ in range(max(1, args.warmup // 2)):
+            bk.dense_prefill(prob, q, kp, vp, out=dout)
+        torch.cuda.synchronize()
+        d0, d1 = ev(), ev()
+        nd = max(2, args.steps // 2)
+        d0.record(stream)
+        for _ in range(nd):
+            bk.dense_prefill(prob, q, kp, vp, out=dout)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / nd
+
+    osk_tflops = osk_flops / (osk_ms * 1e-3) / 1e12 if osk_ms > 0 else 0.0
+    kap_bytes = (q.numel() * 2 + (w.total_tokens * w.num_kv_heads * w.head_dim * 2)
+                 + 2 * mask.blocks.numel() * 4 + mask.counts.numel() * 8)
+    result = {
+        "metric": "128K prefill attention ms/layer (KAP + OSK); speedup vs own dense kernel; "
+                  "MFMA util",
+        "value": round(ms_step, 4),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "seq_lens": list(w.seqlens), "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "q_block": w.q_block,
+                   "page_size": w.page_size, "budget": budget, "tau": tau, "seed": w.seed,
+                   "parallelism": "none (1 GPU)"},
+        "kap_ms": round(kap_ms, 4),
+        "osk_ms": round(osk_ms, 4),
+        "dense_ms": None if dense_ms is None else round(dense_ms, 4),
+        "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
+        "speedup_osk_only_vs_dense": None if dense_ms is None else round(dense_ms / osk_ms, 3),
+        "dense_tflops": None if dense_ms is None else round(dense_flops / dense_ms / 1e9, 1),
+        "dense_mfma_frac": None if dense_ms is None else
+        round(dense_flops / dense_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+        "osk_tflops": round(osk_tflops, 1),
+        "osk_mfma_frac": round(osk_tflops / PEAK_BF16_TFLOPS, 4),
+        "kap_gbs": round(kap_bytes / (kap_ms * 1e-3) / 1e9, 1),
+        "visited_slots": visited, "skipped_slots": skipped, "causal_slots": causal_slots,
+        "stage1_budget": round(visited / causal_slots, 5),
+        "skip_ratio": round(skipped / max(visited, 1), 5),
+        "effective_budget": round(computed / causal_slots, 5),
+        "wall_ms_timed_region": round(wall_ms, 2),
+        "input_gen_s": round(gen_s, 1),
+        "roofline": {"bound": "mfma", "achieved": round(osk_tflops, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(osk_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_fwd_kernel<128,4,ordered> (cosa_osk_prefill)",
+                     "algorithmic_flop_per_launch": osk_flops},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x, budget, tau, args.cpu_tiles)
+    print(json.dumps(result), flush=True)
+
+    if args.sweep and w.budgets_sweep:
+        for b_ in w.budgets_sweep:
+            for t_ in w.taus_sweep:
+                m2 = bk.proxy_ordered_mask(prob, q, kp, b_, workspace=ws)
+                r2 = bk.osk_prefill(prob, q, kp, vp, m2, t_, record=True)
+                torch.cuda.synchronize()
+                st = r2.row_stats.cpu().numpy().reshape(-1, 2)
+                e0, e1, e2 = ev(), ev(), ev()
+                e0.record(stream)
+                for _ in range(args.steps):
+                    bk.proxy_ordered_mask(prob, q, kp, b_, workspace=ws, out=m2)
+                e1.record(stream)
+                for _ in range(args.steps):
+                    bk.osk_prefill(prob, q, kp, vp, m2, t_, out=out)
+                e2.record(stream)
+                torch.cuda.synchronize()
+                km, om = e0.elapsed_time(e1) / args.steps, e1.elapsed_time(e2) / args.steps
+                vis, skp = int(st[:, 0].sum()), int(st[:, 1].sum())
+                fl = fps * (2 * vis - skp)
+                print(json.dumps({"sweep": w.name, "budget": b_, "tau": t_, "kap_ms": round(km, 4),
+                                  "osk_ms": round(om, 4), "ms_per_layer": round(km + om, 4),
+                                  "speedup_vs_dense": None if dense_ms is None else
+                                  round(dense_ms / (km + om), 3),
+                                  "stage1_budget": round(vis / causal_slots, 5),
+                                  "skip_ratio": round(skp / max(vis, 1), 5),
+                                  "osk_tflops": round(fl / om / 1e9, 1)}), flush=True)
+
+
+def cpu_baseline(w, x, budget, tau, n_tiles):
+    """Time the CPU oracle (KAP + OSK closed form) on a bounded, seeded sample
+    of tiles of the same layer and extrapolate by per-tile work."""
+    from oracle import kap as okap
+    from oracle import osk as oosk
+    from oracle.paging import materialise
+
+    threads = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(1234)
+    beta = okap.budget_ppm(budget)
+    grp = w.num_q_heads // w.num_kv_heads
+    b = int(np.argmax(np.diff(x.cu_seqlens)))
+    s0, L = int(x.cu_seqlens[b]), int(np.diff(x.cu_seqlens)[b])
+    nqb = (L + w.q_block - 1) // w.q_block
+    t_prep = time.perf_counter()
+    keys = materialise(x.k_pool, x.page_table[b], L, w.page_size)
+    vals = materialise(x.v_pool, x.page_table[b], L, w.page_size)
+    prep_s = time.perf_counter() - t_prep
+    tiles = sorted(rng.choice(nqb, size=min(n_tiles, nqb), replace=False).tolist())
+    heads = rng.choice(w.num_q_heads, size=len(tiles)).tolist()
+    t0 = time.perf_counter()
+    work_sample = 0.0
+    for i, h in zip(tiles, heads):
+        g = h // grp
+        res = okap.head_tiles(x.q[s0:s0 + L, h].astype(np.float64), keys[:, g], w.softmax_scale,
+                              w.q_block, w.page_size, beta, tiles=[i])[i]
+        rows = np.arange(i * w.q_block, min((i + 1) * w.q_block, L))
+        oosk.osk_tile_closed_form(x.q[s0 + rows, h].astype(np.float64), rows, keys[:, g],
+                                  vals[:, g], res.blocks, tau, w.softmax_scale, w.page_size)
+        work_sample += i + 1
+    t_sample = time.perf_counter() - t0
+    # whole-layer work in the same unit (candidate blocks summed over tiles and heads)
+    total_work = 0.0
+    for L_ in np.diff(x.cu_seqlens):
+        n = (int(L_) + w.q_block - 1) // w.q_block
+        total_work += n * (n + 1) / 2
+    total_work *= w.num_q_heads
+    est_ms = (t_sample / work_sample) * total_work * 1e3 + prep_s * 1e3
+    return {"value": round(est_ms, 1), "unit": "ms/layer", "cores": threads, "kind": "oracle",
+            "sample": f"{len(tiles)} seeded (head, tile) pairs of sequence {b} "
+                      f"(KAP score/sort + OSK closed form, fp64 NumPy), "
+                      f"{t_sample:.1f} s, extrapolated by candidate-block count; "
+                      f"includes {prep_s:.1f} s de-paging"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,9 @@
+"""CoSA block-sparse prefill attention for MI355X (gfx950).
+
+The compute lives in ``libcosa.so`` (hand-written HIP kernels behind the C ABI
+of ``include/cosa.h``); this package is its thin Python binding.  Importing it
+does not load the library; the first call does, and raises if the library has
+not been built (``python -m block_sparse_long_kap_amd.build``).
+"""
+from .api import (KapWorkspace, OrderedMask, PrefillOutput, Problem,  # noqa: F401
+                  dense_prefill, osk_prefill, proxy_ordered_mask, tau_from_delta)

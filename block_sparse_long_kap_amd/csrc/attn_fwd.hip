@@ -1,0 +1,430 @@
+// Paged causal prefill attention for gfx950: the Ordered-Skipping Kernel and
+// the dense baseline share this one kernel template.
+//
+// Method: CoSA (paper text on paperpeel.com), §4.3 "Ordered-Skipping Kernel":
+// the kernel follows the computation-order mask by remapping pages of the
+// paged KV cache (physical jumping, any-order page visiting) and applies the
+// in-kernel skip of §3.3 Eq. (5) at the granularity of one query tile
+// (App. D.1: one tile-wide vote combined from the row-wise predicates, made
+// from the on-chip online-softmax maxima with no extra logits and no extra
+// global-memory traffic).  Dense mode walks every causal block in ascending
+// order through the page table and never votes.
+//
+// gfx950 mapping (one workgroup = one query tile of one query head):
+//   * NW wavefronts of 64 lanes, 32 query rows per wavefront (tile = 32*NW).
+//   * Logits are formed transposed, S^T = K Q^T, with
+//     v_mfma_f32_32x32x16_bf16: each lane then owns one query column and 32
+//     of the 64 keys of a page, so the row max is an in-register reduction
+//     plus one exchange with the partner lane (lane ^ 32).
+//   * The value product is O^T = V^T P^T on the same MFMA: P^T comes straight
+//     from the S^T accumulator registers (rounded to bf16) and the page's V is
+//     staged transposed in LDS, in the key order the accumulator layout
+//     implies.
+//   * K and V^T pages are double-buffered in LDS; the next pages are fetched
+//     into registers while the current one is computed; one workgroup
+//     barrier per visited page carries both the LDS hand-off and the
+//     tile-wide skip vote.
+//   * The tile order is longest-first (tiles with more causal blocks first)
+//     and, when B*Hkv is a multiple of 8, all query heads of one KV head run
+//     on the same XCD so that its K/V pages stay in that XCD's L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cosa_internal.h"
+
+namespace cosa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ float pair_max(float x) {
+  // max over lanes l and l ^ 32
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
+
+// K page in LDS: [64 keys][D] bf16, rows padded by 16 bytes so that the
+// 32 rows one MFMA operand read touches fall into distinct banks while every
+// read of a wavefront stays "one base register + immediate offset".
+template <int D>
+struct KLayout {
+  static constexpr int kStride = D * 2 + 16;
+  static constexpr int kBytes = kPage * kStride;
+  static __device__ __forceinline__ int offset(int row, int chunk16) {
+    return row * kStride + chunk16 * 16;
+  }
+};
+// V^T page in LDS: [D][64 keys] bf16, rows padded by 8 bytes (same reason).
+struct VLayout {
+  static constexpr int kStride = kPage * 2 + 8;
+  static __device__ __forceinline__ int offset(int d, int chunk8) {
+    return d * kStride + chunk8 * 8;
+  }
+};
+
+// Decode the workgroup's (sequence, head, tile): tiles with more causal
+// blocks first; optionally all heads of a KV group on the same XCD.
+__device__ __forceinline__ void decode_tile(const AttnParams& p, int bid, int& b, int& h,
+                                            int& i) {
+  const int hg = p.hq / p.hkv;
+  if (p.xcd_groups > 0) {
+    const int x = bid & 7;
+    const int r = bid >> 3;
+    const int groups_per_xcd = p.xcd_groups >> 3;
+    const int per_level = groups_per_xcd * hg;
+    const int level = r / per_level;
+    const int rem = r - level * per_level;
+    const int gi = rem / hg;
+    const int hh = rem - gi * hg;
+    const int G = x + 8 * gi;
+    b = G / p.hkv;
+    const int g = G - b * p.hkv;
+    h = g * hg + hh;
+    i = p.nqb - 1 - level;
+  } else {
+    const int per_level = p.batch * p.hq;
+    const int level = bid / per_level;
+    const int rem = bid - level * per_level;
+    b = rem / p.hq;
+    h = rem - b * p.hq;
+    i = p.nqb - 1 - level;
+  }
+}
+
+template <int D, int NW, bool kOrdered>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p) {
+  constexpr int NT = NW * 64;
+  constexpr int BQ = NW * 32;
+  constexpr int KCH = D / 8;                         // 16-byte chunks per key row
+  constexpr int K_TOTAL = kPage * KCH;               // 16-byte chunks per K page
+  constexpr int K_PER = (K_TOTAL + NT - 1) / NT;
+  constexpr int V_TOTAL = KCH * (kPage / 4);         // (d-chunk, key-quad) pairs
+  constexpr int V_PER = (V_TOTAL + NT - 1) / NT;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+
+  __shared__ __attribute__((aligned(16))) unsigned char sK[2][KLayout<D>::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sV[2][D * VLayout::kStride];
+  __shared__ int sVote[2][NW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hf = lane >> 5;
+  const int col = lane & 31;
+
+  int b, h, i;
+  decode_tile(p, blockIdx.x, b, h, i);
+  const int hg = p.hq / p.hkv;
+  const int g = h / hg;
+  const int q0 = p.cu_seqlens[b];
+  const int L = p.cu_seqlens[b + 1] - q0;
+  const int tile_q0 = i * BQ;
+  const int64_t row = ((int64_t)b * p.hq + h) * p.nqb + i;
+  if (tile_q0 >= L) {
+    if (kOrdered && p.row_stats != nullptr && tid == 0) {
+      p.row_stats[2 * row] = 0;
+      p.row_stats[2 * row + 1] = 0;
+    }
+    return;
+  }
+  const int tile_last = min(tile_q0 + BQ, L) - 1;
+  const int cnt = kOrdered ? p.counts[row] : tile_last / kPage + 1;
+  const int32_t* ob = kOrdered ? p.ordered_blocks + row * p.capacity : nullptr;
+  const int32_t* op = kOrdered ? p.ordered_pages + row * p.capacity : nullptr;
+  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
+
+  const int wave_q0 = tile_q0 + wave * 32;
+  const int wave_last = min(wave_q0 + 31, L - 1);     // < wave_q0 if the wave has no rows
+  const int qpos = wave_q0 + col;
+  const bool row_valid = qpos < L;
+
+  // ---- Q^T operand (B of S^T = K Q^T), kept in registers for the whole tile
+  bf16x8_t qf[KSTEPS];
+  {
+    const uint16_t* qp = p.q + ((int64_t)(q0 + qpos) * p.hq + h) * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (row_valid) v = *reinterpret_cast<const u32x4_t*>(qp + ks * 16);
+      qf[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  auto slot_block = [&](int t) -> int { return kOrdered ? ob[t] : t; };
+  auto slot_page = [&](int t) -> int { return kOrdered ? op[t] : pt[t]; };
+
+  u32x4_t kreg[K_PER];
+  u32x4_t vreg[V_PER][4];
+
+  auto load_k = [&](int page) {
+    const uint16_t* base = p.k_pool + ((int64_t)page * p.hkv + g) * (kPage * D);
+#pragma unroll
+    for (int e = 0; e < K_PER; ++e) {
+      const int idx = tid + e * NT;
+      if (K_TOTAL % NT == 0 || idx < K_TOTAL) {
+        const int r = idx / KCH, c = idx % KCH;
+        kreg[e] = *reinterpret_cast<const u32x4_t*>(base + r * D + c * 8);
+      }
+    }
+  };
+  auto store_k = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < K_PER; ++e) {
+      const int idx = tid + e * NT;
+      if (K_TOTAL % NT == 0 || idx < K_TOTAL) {
+        const int r = idx / KCH, c = idx % KCH;
+        *reinterpret_cast<u32x4_t*>(&sK[buf][KLayout<D>::offset(r, c)]) = kreg[e];
+      }
+    }
+  };
+  // V: each (d-chunk, key-quad) pair loads 4 keys x 8 dims; keys past the end
+  // of the sequence are replaced by zeros so that unused slots of the last
+  // page (whatever they hold) cannot reach the output through 0 * NaN.
+  auto load_v = [&](int page, int block) {
+    const uint16_t* base = p.v_pool + ((int64_t)page * p.hkv + g) * (kPage * D);
+    const int valid_keys = L - block * kPage;
+#pragma unroll
+    for (int e = 0; e < V_PER; ++e) {
+      const int idx = tid + e * NT;
+      if (V_TOTAL % NT == 0 || idx < V_TOTAL) {
+        const int c = idx % KCH, kq = idx / KCH;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kq * 4 + r;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(base + key * D + c * 8);
+          const bool ok = key < valid_keys;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) vreg[e][r][w] = ok ? v[w] : 0u;
+        }
+      }
+    }
+  };
+  auto store_v = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < V_PER; ++e) {
+      const int idx = tid + e * NT;
+      if (V_TOTAL % NT == 0 || idx < V_TOTAL) {
+        const int c = idx % KCH, kq = idx / KCH;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // dims 2w (low halves) and 2w+1 (high halves) of keys 4kq..4kq+3
+          const uint32_t a0 = vreg[e][0][w], a1 = vreg[e][1][w];
+          const uint32_t a2 = vreg[e][2][w], a3 = vreg[e][3][w];
+          u32x2_t lo, hi;
+          lo[0] = (a0 & 0xFFFFu) | (a1 << 16);
+          lo[1] = (a2 & 0xFFFFu) | (a3 << 16);
+          hi[0] = (a0 >> 16) | (a1 & 0xFFFF0000u);
+          hi[1] = (a2 >> 16) | (a3 & 0xFFFF0000u);
+          const int d = c * 8 + 2 * w;
+          *reinterpret_cast<u32x2_t*>(&sV[buf][VLayout::offset(d, kq)]) = lo;
+          *reinterpret_cast<u32x2_t*>(&sV[buf][VLayout::offset(d + 1, kq)]) = hi;
+        }
+      }
+    }
+  };
+
+  f32x16_t o[DBLK];
+#pragma unroll
+  for (int md = 0; md < DBLK; ++md) o[md] = (f32x16_t){};
+  float m2 = kNegInf;   // running max of this lane's query row, log2 units
+  float lsum = 0.f;     // this lane's half of the running sum
+  int nskip = 0;
+  const bool skip_on = kOrdered && p.tau_log2 >= 0.f;
+
+  int j_cur = 0, j_next = 0;
+  if (cnt > 0) {
+    j_cur = slot_block(0);
+    load_k(slot_page(0));
+    store_k(0);
+    if (cnt > 1) {
+      j_next = slot_block(1);
+      load_k(slot_page(1));
+    }
+    load_v(slot_page(0), j_cur);
+    __syncthreads();
+  }
+
+  for (int t = 0; t < cnt; ++t) {
+    const int buf = t & 1;
+    const int key0 = j_cur * kPage;
+    // some key of the page is visible to some valid row of this wave
+    const bool active = wave_q0 < L && key0 <= wave_last;
+
+    // ---- S^T = K Q^T for this wave's 32 queries
+    f32x16_t s[2];
+    s[0] = (f32x16_t){};
+    s[1] = (f32x16_t){};
+    float bm = kNegInf;
+    if (active) {
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+              &sK[buf][KLayout<D>::offset(mb * 32 + col, 2 * ks + hf)]);
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                          qf[ks], s[mb], 0, 0, 0);
+        }
+      }
+      // causal / end-of-sequence mask: key index in the page > lim is masked
+      const bool need_mask = (key0 + kPage - 1 > wave_q0) || (key0 + kPage > L);
+      const int lim = min(qpos, L - 1) - key0 - 4 * hf;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int koff = mb * 32 + 8 * (r >> 2) + (r & 3);   // compile-time
+          float v = s[mb][r] * p.scale_log2;
+          v = (need_mask && koff > lim) ? kNegInf : v;
+          s[mb][r] = v;
+          bm = fmaxf(bm, v);
+        }
+      }
+      bm = pair_max(bm);
+    }
+
+    // ---- tile-wide vote: every valid row must find the block negligible
+    if (skip_on) {
+      const bool pred = !row_valid || (bm < m2 - p.tau_log2);
+      const bool wave_all = __all(pred);
+      if (lane == 0) sVote[buf][wave] = wave_all ? 1 : 0;
+    }
+
+    // ---- hand the next K page and this V page to LDS; one barrier per page
+    if (t + 1 < cnt) store_k(buf ^ 1);
+    store_v(buf);
+    __syncthreads();
+
+    bool skip = false;
+    if (skip_on) {
+      int all = 1;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) all &= sVote[buf][w];
+      skip = all != 0;
+    }
+
+    // ---- prefetch K(t+2) and V(t+1) into registers
+    const int j_after = j_next;
+    if (t + 2 < cnt) {
+      j_next = slot_block(t + 2);
+      load_k(slot_page(t + 2));
+    }
+    if (t + 1 < cnt) load_v(slot_page(t + 1), j_after);
+
+    if (skip) {
+      ++nskip;
+      if (p.skip_record != nullptr && tid == 0) p.skip_record[row * p.capacity + t] = 1;
+      j_cur = j_after;
+      continue;
+    }
+    if (kOrdered && p.skip_record != nullptr && tid == 0) p.skip_record[row * p.capacity + t] = 0;
+
+    if (active) {
+      // ---- online softmax update (log2 domain)
+      const float mn = fmaxf(m2, bm);
+      const float alpha = (m2 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+      const float mu = (mn == kNegInf) ? 0.f : mn;
+      float part = 0.f;
+      bf16x8_t pb[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(s[mb][r] - mu);
+          part += e;
+          pb[mb * 2 + (r >> 3)][r & 7] = (__bf16)e;
+        }
+      }
+      lsum = alpha * lsum + part;
+      m2 = mn;
+#pragma unroll
+      for (int md = 0; md < DBLK; ++md) o[md] *= alpha;
+
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int md = 0; md < DBLK; ++md) {
+          const int d = md * 32 + col;
+          u32x4_t a;
+          const u32x2_t a0 =
+              *reinterpret_cast<const u32x2_t*>(&sV[buf][VLayout::offset(d, 4 * ks + hf)]);
+          const u32x2_t a1 =
+              *reinterpret_cast<const u32x2_t*>(&sV[buf][VLayout::offset(d, 4 * ks + 2 + hf)]);
+          a[0] = a0[0];
+          a[1] = a0[1];
+          a[2] = a1[0];
+          a[3] = a1[1];
+          o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                          pb[ks], o[md], 0, 0, 0);
+        }
+      }
+    }
+    j_cur = j_after;
+  }
+
+  // ---- epilogue: out = O / l, lse = m + ln l
+  const float ltot = pair_sum(lsum);
+  if (row_valid) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    uint16_t* dst = p.out + ((int64_t)(q0 + qpos) * p.hq + h) * D;
+#pragma unroll
+    for (int md = 0; md < DBLK; ++md) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d = md * 32 + 8 * rq + 4 * hf;
+        __bf16 v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[md][4 * rq + e] * inv);
+        u32x2_t w;
+        w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v4[0]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, v4[1]) << 16);
+        w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v4[2]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, v4[3]) << 16);
+        *reinterpret_cast<u32x2_t*>(dst + d) = w;
+      }
+    }
+    if (p.lse != nullptr && hf == 0) {
+      p.lse[(int64_t)h * p.total_q + q0 + qpos] =
+          ltot > 0.f ? (m2 + __log2f(ltot)) * kLn2 : kNegInf;
+    }
+  }
+  if (kOrdered && p.row_stats != nullptr && tid == 0) {
+    p.row_stats[2 * row] = cnt;
+    p.row_stats[2 * row + 1] = nskip;
+  }
+}
+
+template <int D, int NW, bool kOrdered>
+hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
+  const int64_t grid = (int64_t)p.batch * p.hq * p.nqb;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, kOrdered>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, bool ordered,
+                            hipStream_t stream) {
+#define COSA_ATTN_CASE(D_, BQ_)                                                       \
+  if (head_dim == D_ && q_block == BQ_)                                               \
+    return ordered ? launch_one<D_, BQ_ / 32, true>(p, stream)                        \
+                   : launch_one<D_, BQ_ / 32, false>(p, stream);
+  COSA_ATTN_CASE(128, 128)
+  COSA_ATTN_CASE(128, 64)
+  COSA_ATTN_CASE(64, 128)
+  COSA_ATTN_CASE(64, 64)
+#undef COSA_ATTN_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cosa

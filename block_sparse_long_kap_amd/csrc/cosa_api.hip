@@ -1,0 +1,251 @@
+// Host side of the C ABI declared in include/cosa.h: argument validation,
+// sizing and kernel launches.  No allocation, no synchronisation, no state
+// between calls other than a thread-local text for the last error.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "cosa.h"
+#include "cosa_internal.h"
+
+#define COSA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+cosa_status fail(cosa_status st, const char* msg) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+  return st;
+}
+cosa_status ok() {
+  g_last_error[0] = '\0';
+  return COSA_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool budget_to_ppm(float budget, int32_t* ppm) {
+  if (!(budget > 0.f) || !(budget <= 1.f)) return false;
+  const double v = floor((double)budget * 1e6 + 0.5);
+  *ppm = (int32_t)(v < 1.0 ? 1.0 : v);
+  return true;
+}
+
+int64_t budget_count(int64_t n, int32_t ppm) {
+  if (n <= 0) return 0;
+  int64_t k = (n * ppm + 999999) / 1000000;
+  if (k < 1) k = 1;
+  if (k > n) k = n;
+  return k;
+}
+
+cosa_status validate(const cosa_problem* p) {
+  if (p == nullptr) return fail(COSA_ERR_INVALID_ARG, "problem is null");
+  if (p->batch < 1) return fail(COSA_ERR_INVALID_ARG, "batch must be >= 1");
+  if (p->num_kv_heads < 1 || p->num_q_heads < 1 || p->num_q_heads % p->num_kv_heads != 0)
+    return fail(COSA_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(COSA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (p->q_block != 64 && p->q_block != 128)
+    return fail(COSA_ERR_UNSUPPORTED, "q_block must be 64 or 128");
+  if (p->page_size != cosa::kPage) return fail(COSA_ERR_UNSUPPORTED, "page_size must be 64");
+  if (p->kv_block != p->page_size)
+    return fail(COSA_ERR_UNSUPPORTED, "kv_block must equal page_size");
+  if (p->max_seqlen < 1 || p->max_seqlen > (1 << 20))
+    return fail(COSA_ERR_INVALID_ARG, "max_seqlen must lie in [1, 2^20]");
+  if (p->max_pages_per_seq < ceil_div(p->max_seqlen, p->page_size))
+    return fail(COSA_ERR_INVALID_ARG, "max_pages_per_seq < ceil(max_seqlen / page_size)");
+  if (p->num_pages < 1) return fail(COSA_ERR_INVALID_ARG, "num_pages must be >= 1");
+  if (p->total_q < 0 || p->total_q > (int64_t)p->batch * p->max_seqlen)
+    return fail(COSA_ERR_INVALID_ARG, "total_q must lie in [0, batch * max_seqlen]");
+  if (!(p->softmax_scale > 0.f) || !isfinite(p->softmax_scale))
+    return fail(COSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (p->cu_seqlens == nullptr || p->page_table == nullptr)
+    return fail(COSA_ERR_INVALID_ARG, "cu_seqlens and page_table must be non-null");
+  const int64_t grid = (int64_t)p->batch * p->num_q_heads * ceil_div(p->max_seqlen, p->q_block);
+  if (grid > 0x7FFFFFFFLL) return fail(COSA_ERR_UNSUPPORTED, "too many query tiles");
+  return ok();
+}
+
+cosa_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return ok();
+  return fail(COSA_ERR_HIP, hipGetErrorString(e));
+}
+
+int32_t xcd_groups(const cosa_problem* p) {
+  const int64_t groups = (int64_t)p->batch * p->num_kv_heads;
+  return (groups % 8 == 0 && groups <= 0x7FFFFFFF) ? (int32_t)groups : 0;
+}
+
+void fill_attn(cosa::AttnParams& a, const cosa_problem* p, const void* q, const void* k_pool,
+               const void* v_pool, void* out, float* lse) {
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = static_cast<const uint16_t*>(k_pool);
+  a.v_pool = static_cast<const uint16_t*>(v_pool);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.cu_seqlens = p->cu_seqlens;
+  a.page_table = p->page_table;
+  a.ordered_blocks = nullptr;
+  a.ordered_pages = nullptr;
+  a.counts = nullptr;
+  a.skip_record = nullptr;
+  a.row_stats = nullptr;
+  a.capacity = 0;
+  a.total_q = p->total_q;
+  a.batch = p->batch;
+  a.hq = p->num_q_heads;
+  a.hkv = p->num_kv_heads;
+  a.max_pages = p->max_pages_per_seq;
+  a.nqb = (int32_t)ceil_div(p->max_seqlen, p->q_block);
+  a.xcd_groups = xcd_groups(p);
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.tau_log2 = -1.f;
+}
+
+}  // namespace
+
+COSA_EXPORT int32_t cosa_abi_version(void) { return COSA_ABI_VERSION; }
+
+COSA_EXPORT const char* cosa_status_string(cosa_status s) {
+  switch (s) {
+    case COSA_OK: return "COSA_OK";
+    case COSA_ERR_INVALID_ARG: return "COSA_ERR_INVALID_ARG";
+    case COSA_ERR_UNSUPPORTED: return "COSA_ERR_UNSUPPORTED";
+    case COSA_ERR_WORKSPACE: return "COSA_ERR_WORKSPACE";
+    case COSA_ERR_HIP: return "COSA_ERR_HIP";
+  }
+  return "COSA_ERR_UNKNOWN";
+}
+
+COSA_EXPORT const char* cosa_last_error(void) { return g_last_error; }
+
+COSA_EXPORT cosa_status cosa_validate_problem(const cosa_problem* p) { return validate(p); }
+
+COSA_EXPORT int64_t cosa_num_q_tiles(const cosa_problem* p) {
+  const cosa_status st = validate(p);
+  if (st != COSA_OK) return st;
+  return ceil_div(p->max_seqlen, p->q_block);
+}
+
+COSA_EXPORT int64_t cosa_mask_capacity(const cosa_problem* p, float budget) {
+  const cosa_status st = validate(p);
+  if (st != COSA_OK) return st;
+  int32_t ppm;
+  if (!budget_to_ppm(budget, &ppm)) return fail(COSA_ERR_INVALID_ARG, "budget must lie in (0, 1]");
+  return budget_count(ceil_div(p->max_seqlen, p->kv_block), ppm);
+}
+
+COSA_EXPORT size_t cosa_kap_workspace_size(const cosa_problem* p) {
+  if (validate(p) != COSA_OK) return 0;
+  const int64_t n_max = ceil_div(p->max_seqlen, p->kv_block);
+  return (size_t)p->batch * p->num_kv_heads * p->head_dim * n_max * sizeof(float);
+}
+
+COSA_EXPORT cosa_status cosa_check_page_table_host(const cosa_problem* p,
+                                                   const int32_t* cu_host,
+                                                   const int32_t* table_host) {
+  cosa_status st = validate(p);
+  if (st != COSA_OK) return st;
+  if (cu_host == nullptr || table_host == nullptr)
+    return fail(COSA_ERR_INVALID_ARG, "host arrays must be non-null");
+  if (cu_host[0] != 0) return fail(COSA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+  for (int b = 0; b < p->batch; ++b) {
+    const int64_t len = (int64_t)cu_host[b + 1] - cu_host[b];
+    if (len < 0) return fail(COSA_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing");
+    if (len > p->max_seqlen) return fail(COSA_ERR_INVALID_ARG, "a sequence exceeds max_seqlen");
+    const int64_t pages = ceil_div(len, p->page_size);
+    for (int64_t j = 0; j < pages; ++j) {
+      const int32_t pg = table_host[(int64_t)b * p->max_pages_per_seq + j];
+      if (pg < 0 || pg >= p->num_pages)
+        return fail(COSA_ERR_INVALID_ARG, "page id out of [0, num_pages)");
+    }
+  }
+  if (cu_host[p->batch] != p->total_q)
+    return fail(COSA_ERR_INVALID_ARG, "cu_seqlens[batch] != total_q");
+  return ok();
+}
+
+COSA_EXPORT cosa_status cosa_proxy_ordered_mask(const cosa_problem* p, const void* q,
+                                                const void* k_pool, float budget,
+                                                int32_t* ordered_blocks, int32_t* ordered_pages,
+                                                int32_t* counts, int32_t* hrm_counts,
+                                                float* debug_w, uint8_t* debug_hrm,
+                                                int64_t capacity, void* workspace,
+                                                size_t workspace_bytes, void* stream) {
+  cosa_status st = validate(p);
+  if (st != COSA_OK) return st;
+  if (q == nullptr || k_pool == nullptr || ordered_blocks == nullptr ||
+      ordered_pages == nullptr || counts == nullptr)
+    return fail(COSA_ERR_INVALID_ARG, "q, k_pool, ordered_blocks, ordered_pages, counts required");
+  int32_t ppm;
+  if (!budget_to_ppm(budget, &ppm)) return fail(COSA_ERR_INVALID_ARG, "budget must lie in (0, 1]");
+  const int64_t n_max = ceil_div(p->max_seqlen, p->kv_block);
+  if (n_max > cosa::kMaxCandidates)
+    return fail(COSA_ERR_UNSUPPORTED, "the proxy handles at most 2048 key blocks per sequence");
+  if (capacity < budget_count(n_max, ppm))
+    return fail(COSA_ERR_INVALID_ARG, "capacity < cosa_mask_capacity(problem, budget)");
+  const size_t need = cosa_kap_workspace_size(p);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(COSA_ERR_WORKSPACE, "workspace null or smaller than cosa_kap_workspace_size()");
+  cosa::KapParams k;
+  k.q = static_cast<const uint16_t*>(q);
+  k.k_pool = static_cast<const uint16_t*>(k_pool);
+  k.cu_seqlens = p->cu_seqlens;
+  k.page_table = p->page_table;
+  k.kbar = static_cast<float*>(workspace);
+  k.ordered_blocks = ordered_blocks;
+  k.ordered_pages = ordered_pages;
+  k.counts = counts;
+  k.hrm_counts = hrm_counts;
+  k.debug_w = debug_w;
+  k.debug_hrm = debug_hrm;
+  k.capacity = capacity;
+  k.batch = p->batch;
+  k.hq = p->num_q_heads;
+  k.hkv = p->num_kv_heads;
+  k.max_pages = p->max_pages_per_seq;
+  k.nqb = (int32_t)ceil_div(p->max_seqlen, p->q_block);
+  k.n_max = (int32_t)n_max;
+  k.beta_ppm = ppm;
+  k.scale = p->softmax_scale;
+  return hip_status(cosa::launch_kap(k, p->head_dim, p->q_block, (hipStream_t)stream));
+}
+
+COSA_EXPORT cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, const void* k_pool,
+                                         const void* v_pool, const int32_t* ordered_blocks,
+                                         const int32_t* ordered_pages, const int32_t* counts,
+                                         int64_t capacity, float skip_tau, void* out, float* lse,
+                                         uint8_t* skip_record, int32_t* row_stats, void* stream) {
+  cosa_status st = validate(p);
+  if (st != COSA_OK) return st;
+  if (q == nullptr || k_pool == nullptr || v_pool == nullptr || out == nullptr ||
+      ordered_blocks == nullptr || ordered_pages == nullptr || counts == nullptr)
+    return fail(COSA_ERR_INVALID_ARG, "q, k_pool, v_pool, out and the mask arrays are required");
+  if (capacity < 1) return fail(COSA_ERR_INVALID_ARG, "capacity must be >= 1");
+  if (isnan(skip_tau)) return fail(COSA_ERR_INVALID_ARG, "skip_tau is NaN");
+  cosa::AttnParams a;
+  fill_attn(a, p, q, k_pool, v_pool, out, lse);
+  a.ordered_blocks = ordered_blocks;
+  a.ordered_pages = ordered_pages;
+  a.counts = counts;
+  a.skip_record = skip_record;
+  a.row_stats = row_stats;
+  a.capacity = capacity;
+  a.tau_log2 = skip_tau < 0.f ? -1.f : skip_tau * 1.4426950408889634f;
+  return hip_status(cosa::launch_attention(a, p->head_dim, p->q_block, true, (hipStream_t)stream));
+}
+
+COSA_EXPORT cosa_status cosa_dense_prefill(const cosa_problem* p, const void* q,
+                                           const void* k_pool, const void* v_pool, void* out,
+                                           float* lse, void* stream) {
+  cosa_status st = validate(p);
+  if (st != COSA_OK) return st;
+  if (q == nullptr || k_pool == nullptr || v_pool == nullptr || out == nullptr)
+    return fail(COSA_ERR_INVALID_ARG, "q, k_pool, v_pool and out are required");
+  cosa::AttnParams a;
+  fill_attn(a, p, q, k_pool, v_pool, out, lse);
+  return hip_status(cosa::launch_attention(a, p->head_dim, p->q_block, false, (hipStream_t)stream));
+}

@@ -1,0 +1,58 @@
+// Internal declarations shared by the host API and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cosa {
+
+constexpr int kPage = 64;          // tokens per KV page == logical key block
+constexpr int kProxyRows = 16;     // query rows pooled into one proxy row
+constexpr int kMaxCandidates = 2048;  // KAP: key blocks per tile handled in one pass
+
+// Arguments of the attention kernel (dense and ordered-skipping modes).
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  uint16_t* out;
+  float* lse;
+  const int32_t* cu_seqlens;
+  const int32_t* page_table;
+  const int32_t* ordered_blocks;  // OSK only
+  const int32_t* ordered_pages;   // OSK only
+  const int32_t* counts;          // OSK only
+  uint8_t* skip_record;           // OSK only, nullable
+  int32_t* row_stats;             // OSK only, nullable
+  int64_t capacity;
+  int64_t total_q;
+  int32_t batch, hq, hkv, max_pages, nqb;
+  int32_t xcd_groups;             // >0: B*Hkv, a multiple of 8 -> XCD-affine order
+  float scale_log2;               // softmax_scale * log2(e)
+  float tau_log2;                 // skip threshold * log2(e); < 0 disables
+};
+
+// Arguments of the two KAP kernels.
+struct KapParams {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const int32_t* cu_seqlens;
+  const int32_t* page_table;
+  float* kbar;                    // workspace fp32 [B][Hkv][D][n_max]
+  int32_t* ordered_blocks;
+  int32_t* ordered_pages;
+  int32_t* counts;
+  int32_t* hrm_counts;            // nullable
+  float* debug_w;                 // nullable [rows][n_max]
+  uint8_t* debug_hrm;             // nullable [rows][n_max]
+  int64_t capacity;
+  int32_t batch, hq, hkv, max_pages, nqb, n_max;
+  int32_t beta_ppm;
+  float scale;
+};
+
+hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, bool ordered,
+                            hipStream_t stream);
+hipError_t launch_kap(const KapParams& p, int head_dim, int q_block, hipStream_t stream);
+
+}  // namespace cosa

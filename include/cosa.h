@@ -1,0 +1,194 @@
+/*
+ * cosa.h - C ABI of a gfx950 (MI355X) library for CoSA block-sparse causal
+ * prefill attention over a paged KV cache.
+ *
+ * The method is described in "CoSA: Accelerating Long-Context Inference via
+ * Proxy-Kernel Co-Designed Sparse Attention" (paper text on paperpeel.com):
+ *   - the Kernel-Aware Proxy (KAP, §4.2 and App. C.1) scores key blocks for
+ *     every query block and emits a computation-order mask M_KAP, with the
+ *     "have rowmax" (HRM) blocks first, truncated to a stage-1 budget;
+ *   - the Ordered-Skipping Kernel (OSK, §4.3) visits only the pages of that
+ *     mask, in its order, through the page table ("physical jumping over
+ *     pages", "any-order page visiting"), and skips the value-side work of a
+ *     block from the exact online-softmax statistics ("in-kernel logic skip",
+ *     §3.3 Eq. (5)) with one vote per query tile (App. D.1);
+ *   - dense causal prefill (§3.1; the full-attention baseline of §5.1) runs on
+ *     the same kernel with every causal block visited in ascending order.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers named "device" point to GPU memory; the library never allocates,
+ * frees or synchronises, keeps no state between calls and enqueues all of its
+ * work on the caller's stream (``stream`` is a hipStream_t; NULL is the
+ * default stream).  The caller owns every buffer.  Arguments are validated on
+ * the host before any launch: an invalid call returns an error status and
+ * enqueues nothing.  A launch failure returns COSA_ERR_HIP.  Only host-side
+ * values are checked; device contents (page ids, sequence lengths in
+ * cu_seqlens) are trusted, see cosa_check_page_table_host().
+ *
+ * Layouts (row-major, innermost last):
+ *   q, out     bf16  [total_q][num_q_heads][head_dim]   packed sequences
+ *   k_pool,
+ *   v_pool     bf16  [num_pages][num_kv_heads][page_size][head_dim]
+ *   cu_seqlens int32 [batch+1]   prefix sums of sequence lengths (device)
+ *   page_table int32 [batch][max_pages_per_seq] logical block -> page (device)
+ *   lse        fp32  [num_q_heads][total_q]   natural-log sum-exp per row
+ * Prefill: every sequence's query length equals its key length, the causal
+ * mask admits key u for query t iff u <= t.  Grouped-query attention: query
+ * head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Mask layout: "mask rows" are indexed row = (b * num_q_heads + h) * NQB + i
+ * with NQB = cosa_num_q_tiles(); a mask row holds ``capacity`` int32 slots,
+ * slot t at [row * capacity + t].
+ */
+#ifndef COSA_H_
+#define COSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  COSA_OK = 0,
+  COSA_ERR_INVALID_ARG = -1, /* a host-checkable argument is out of range */
+  COSA_ERR_UNSUPPORTED = -2, /* valid but not built (e.g. head_dim 96)    */
+  COSA_ERR_WORKSPACE = -3,   /* workspace pointer null or too small       */
+  COSA_ERR_HIP = -4          /* the HIP runtime reported a launch error    */
+} cosa_status;
+
+/* One attention layer's prefill problem.  All scalars are host values. */
+typedef struct {
+  int32_t batch;             /* number of sequences, >= 1                  */
+  int32_t num_q_heads;       /* Hq, multiple of num_kv_heads               */
+  int32_t num_kv_heads;      /* Hkv >= 1                                   */
+  int32_t head_dim;          /* 64 or 128                                  */
+  int32_t q_block;           /* query tile rows: 64 or 128                 */
+  int32_t kv_block;          /* logical key block: must equal page_size    */
+  int32_t page_size;         /* tokens per KV page: 64                     */
+  int32_t max_seqlen;        /* >= every sequence length, <= 1 << 20       */
+  int32_t max_pages_per_seq; /* page_table row stride, >= ceil(max_seqlen / page_size) */
+  int32_t num_pages;         /* pages in the pool                          */
+  int64_t total_q;           /* cu_seqlens[batch]                          */
+  float softmax_scale;       /* > 0, usually 1/sqrt(head_dim)              */
+  const int32_t* cu_seqlens; /* device [batch+1]                           */
+  const int32_t* page_table; /* device [batch][max_pages_per_seq]          */
+} cosa_problem;
+
+/* ABI version of this header (bumped on any incompatible change). */
+#define COSA_ABI_VERSION 1
+int32_t cosa_abi_version(void);
+
+/* Static text for a status code. */
+const char* cosa_status_string(cosa_status status);
+
+/* Text describing the last error returned on the calling thread ("" if none). */
+const char* cosa_last_error(void);
+
+/* Validates the host fields of ``p``.  Returns COSA_OK, COSA_ERR_INVALID_ARG
+ * or COSA_ERR_UNSUPPORTED. */
+cosa_status cosa_validate_problem(const cosa_problem* p);
+
+/* NQB: query tiles of the longest sequence, ceil(max_seqlen / q_block)
+ * (at least 1).  Returns a negative cosa_status on an invalid problem. */
+int64_t cosa_num_q_tiles(const cosa_problem* p);
+
+/* Mask capacity C: the largest number of blocks the KAP can keep for any
+ * tile, clamp(ceil(n_max * beta), 1, n_max) with n_max = ceil(max_seqlen /
+ * kv_block) and beta = floor(budget * 1e6 + 0.5) / 1e6 (integer parts per
+ * million, CoSA (paperpeel) §4.1 "stage-1 budget").  budget must lie in
+ * (0, 1].  Returns a negative cosa_status on error. */
+int64_t cosa_mask_capacity(const cosa_problem* p, float budget);
+
+/* Bytes of device workspace cosa_proxy_ordered_mask() needs (pooled keys,
+ * fp32 [batch][num_kv_heads][head_dim][n_max]).  0 on an invalid problem. */
+size_t cosa_kap_workspace_size(const cosa_problem* p);
+
+/* Host-side check of a host copy of cu_seqlens [batch+1] and page_table
+ * [batch][max_pages_per_seq]: lengths non-decreasing prefix sums ending at
+ * total_q, each length <= max_seqlen, and every page id a sequence uses in
+ * [0, num_pages).  Reads only host memory. */
+cosa_status cosa_check_page_table_host(const cosa_problem* p, const int32_t* cu_seqlens_host,
+                                       const int32_t* page_table_host);
+
+/*
+ * Kernel-Aware Proxy: ordered computation mask M_KAP (CoSA (paperpeel) §4.1,
+ * §4.2 "Block ranking" / "Flag-grouped sorting", App. C.1; fused scoring and
+ * pooling, §5.1 "Implementation details").
+ *
+ * For every mask row (sequence b, query head h, tile i of q_block rows):
+ *   proxy rows: the tile's queries are pooled in groups of 16 consecutive
+ *     rows (mean over the valid rows) and every key block of kv_block keys is
+ *     pooled into its mean key;
+ *   score s[r][j] = softmax_scale * <qbar_r, kbar_j> for the key blocks whose
+ *     first key is at or before proxy row r's last query;
+ *   importance w_j = mean over the tile's proxy rows of softmax_j(s[r][.]);
+ *   HRM_j = j is the (lowest-index) arg-max of s[r][.] for some r;
+ *   order: HRM blocks first, each group by w descending then j ascending;
+ *   kept: the first k = clamp(ceil(n * beta), 1, n) entries of that order,
+ *     with n the tile's candidate count (beta as in cosa_mask_capacity).
+ *
+ * Outputs (device, int32, per mask row; slots past the count are set to -1):
+ *   ordered_blocks [rows][capacity]  logical key block ids in visiting order
+ *   ordered_pages  [rows][capacity]  page_table[b][ordered_blocks[...]]
+ *   counts         [rows]            k (0 for tiles past a sequence's end)
+ *   hrm_counts     [rows] nullable   number of HRM blocks among the kept ones
+ *                                    (they are its first hrm_counts slots)
+ *   debug_w        [rows][n_max] nullable fp32 importance w_j (0 past n)
+ *   debug_hrm      [rows][n_max] nullable uint8 HRM flags
+ * ``capacity`` must be >= cosa_mask_capacity(p, budget).  ``workspace`` must
+ * hold cosa_kap_workspace_size(p) bytes (device, any contents).
+ */
+cosa_status cosa_proxy_ordered_mask(const cosa_problem* p, const void* q, const void* k_pool,
+                                    float budget, int32_t* ordered_blocks,
+                                    int32_t* ordered_pages, int32_t* counts,
+                                    int32_t* hrm_counts, float* debug_w, uint8_t* debug_hrm,
+                                    int64_t capacity, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
+ * Ordered-Skipping Kernel (CoSA (paperpeel) §4.3, App. D.1; skip rule §3.3).
+ *
+ * For every mask row (b, h, i) the kernel walks slots t = 0..counts[row]-1 in
+ * order, fetching key/value page ordered_pages[row][t] (logical block
+ * ordered_blocks[row][t], used for the causal mask), forms the exact logits
+ * S = softmax_scale * Q K^T of the tile, and keeps the online-softmax running
+ * max m and sum l per query row.  If skip_tau >= 0 and every valid row r of
+ * the tile has max_c S[r][c] < m_r - skip_tau (the running max before the
+ * block; -inf < -inf is false), the block's value side (softmax weights,
+ * l and O updates, the V page read from LDS) is skipped.  skip_tau < 0 turns
+ * the skip off (Delta = -1 in App. D.1).  Blocks may come in any order (the
+ * result of online softmax does not depend on it, §3.2).
+ *
+ * out        device bf16 [total_q][Hq][D]: softmax-weighted values over the
+ *            computed keys; 0 for a row that saw no key.
+ * lse        device fp32 [Hq][total_q] nullable: log-sum-exp (natural log)
+ *            over the computed keys, -inf for a row that saw no key.
+ * skip_record device uint8 [rows][capacity] nullable: 1 if slot t was
+ *            skipped in-kernel, 0 if computed; slots past the count untouched.
+ * row_stats  device int32 [rows][2] nullable: (visited slots, skipped slots).
+ * Every listed block id must lie in [0, ceil(L_b / kv_block)) for its
+ * sequence and every page id in [0, num_pages).
+ */
+cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* ordered_blocks,
+                             const int32_t* ordered_pages, const int32_t* counts,
+                             int64_t capacity, float skip_tau, void* out, float* lse,
+                             uint8_t* skip_record, int32_t* row_stats, void* stream);
+
+/*
+ * Dense causal prefill on the same kernel: every tile visits all of its
+ * causal key blocks j = 0 .. (last row) / kv_block in ascending order through
+ * page_table, with no in-kernel skip (CoSA (paperpeel) §3.1, FlashAttention-2
+ * baseline of §5.1).  out / lse as for cosa_osk_prefill().
+ */
+cosa_status cosa_dense_prefill(const cosa_problem* p, const void* q, const void* k_pool,
+                               const void* v_pool, void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COSA_H_ */

@@ -1,0 +1,228 @@
+"""GPU parity: every kernel through the C ABI against the CPU fp64 oracle.
+
+Inputs are seeded synthetic workloads (cosa_inputs), rounded to bf16 once;
+the GPU gets the bf16 tensors, the oracle the same values widened to fp64.
+Tolerances: max-abs 2e-2 / mean-abs 2e-3 on outputs for the same visited set;
+masks and page remaps bit-exact except near-ties of the oracle's own scores;
+skip sets identical except slots within 1e-3 nats of the threshold (counted).
+"""
+import numpy as np
+import pytest
+
+import block_sparse_long_kap_amd as bk
+import cosa_inputs as ci
+from oracle import dense as odense
+from oracle import kap as okap
+from oracle import osk as oosk
+from oracle.paging import materialise
+
+from .parity import ErrStats, check_kap_row, check_osk_tile, upload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _inputs(name, **kw):
+    w = ci.get(name)
+    if kw:
+        w = w.with_(**kw)
+    return w, ci.make(w).bf16_rounded()
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def _dense_oracle(x, w):
+    out = np.zeros(x.q.shape)
+    lse = np.full((w.num_q_heads, x.q.shape[0]), -np.inf)
+    for b in range(w.batch):
+        s, L = int(x.cu_seqlens[b]), int(x.seqlens[b])
+        if L == 0:
+            continue
+        k = materialise(x.k_pool, x.page_table[b], L, w.page_size)
+        v = materialise(x.v_pool, x.page_table[b], L, w.page_size)
+        o, ls = odense.dense_causal_attention(x.q[s:s + L].astype(np.float64), k, v,
+                                              w.softmax_scale)
+        out[s:s + L] = o
+        lse[:, s:s + L] = ls
+    return out, lse
+
+
+RAGGED = dict(seqlens=(1, 63, 64, 65, 200, 383), num_q_heads=8, num_kv_heads=2,
+              head_dim=128, q_block=128, shuffled_pages=True, spare_pages=7,
+              precision="bf16")
+
+
+@pytest.mark.parametrize("case", [
+    ("tiny", {}),
+    ("tiny", dict(RAGGED)),
+    ("tiny", dict(RAGGED, q_block=64)),
+    ("tiny", dict(RAGGED, head_dim=64, q_block=128)),
+])
+def test_dense_matches_oracle(case):
+    name, kw = case
+    w, x = _inputs(name, **kw)
+    print(f"[case] dense {name} {kw}", flush=True)
+    prob, q, k, v = upload(x, DEV)
+    res = bk.dense_prefill(prob, q, k, v)
+    torch.cuda.synchronize()
+    ref, ref_lse = _dense_oracle(x, w)
+    st, ls = ErrStats(), ErrStats()
+    st.add(_np(res.out), ref)
+    ls.add(_np(res.lse), ref_lse)
+    st.assert_ok(label=f"dense {name} out")
+    ls.assert_ok(max_abs=1e-3, mean_abs=1e-4, label=f"dense {name} lse")
+
+
+def _run_osk_vs_oracle(w, x, blocks, counts, tau, label, tiles=None):
+    prob, q, k, v = upload(x, DEV)
+    C = blocks.shape[-1]
+    pages = np.where(blocks >= 0, 0, -1).astype(np.int32)
+    for b in range(w.batch):
+        sel = blocks[b] >= 0
+        pages[b][sel] = x.page_table[b][blocks[b][sel]]
+    mask = bk.OrderedMask(blocks=torch.from_numpy(blocks).to(DEV),
+                          pages=torch.from_numpy(pages).to(DEV),
+                          counts=torch.from_numpy(counts).to(DEV), hrm_counts=None, capacity=C)
+    res = bk.osk_prefill(prob, q, k, v, mask, tau)
+    torch.cuda.synchronize()
+    out, lse, rec, stats = _np(res.out), _np(res.lse), _np(res.skip_record), _np(res.row_stats)
+    st, ls = ErrStats(), ErrStats()
+    near_total = 0
+    n_skipped = 0
+    grp = w.num_q_heads // w.num_kv_heads
+    for b in range(w.batch):
+        s0, L = int(x.cu_seqlens[b]), int(x.seqlens[b])
+        if L == 0:
+            continue
+        kk = materialise(x.k_pool, x.page_table[b], L, w.page_size)
+        vv = materialise(x.v_pool, x.page_table[b], L, w.page_size)
+        nqb = (L + w.q_block - 1) // w.q_block
+        for h in range(w.num_q_heads):
+            g = h // grp
+            for i in range(nqb):
+                if tiles is not None and (b, h, i) not in tiles:
+                    continue
+                rows = np.arange(i * w.q_block, min((i + 1) * w.q_block, L))
+                cnt = int(counts[b, h, i])
+                bl = blocks[b, h, i, :cnt]
+                qr = x.q[s0 + rows, h].astype(np.float64)
+                r = oosk.osk_tile_closed_form(qr, rows, kk[:, g], vv[:, g], bl, tau,
+                                              w.softmax_scale, w.page_size)
+                near_total += check_osk_tile(out[s0 + rows, h], lse[h, s0 + rows],
+                                             rec[b, h, i], r, qr, rows, kk[:, g], vv[:, g], bl,
+                                             w.softmax_scale, w.page_size, st, ls)
+                n_skipped += int(rec[b, h, i, :cnt].sum())
+                assert stats[b, h, i, 0] == cnt
+                assert stats[b, h, i, 1] == int(rec[b, h, i, :cnt].sum())
+    print(f"[parity] {label}: in-kernel skipped slots={n_skipped} near-threshold={near_total}")
+    st.assert_ok(label=f"{label} out")
+    ls.assert_ok(max_abs=1e-3, mean_abs=1e-4, label=f"{label} lse")
+    return n_skipped
+
+
+@pytest.mark.parametrize("case", [("tiny", {}), ("tiny", dict(RAGGED))])
+def test_osk_full_budget_skip_off_equals_dense(case):
+    name, kw = case
+    w, x = _inputs(name, **kw)
+    print(f"[case] osk full budget {name} {kw}", flush=True)
+    blocks, counts = oosk.dense_order_mask(x.cu_seqlens, w.num_q_heads, w.q_block, w.page_size)
+    _run_osk_vs_oracle(w, x, blocks, counts, -1.0, f"osk-full {name}")
+
+
+@pytest.mark.parametrize("tau", [-1.0, 0.0, 4.0, 8.0])
+def test_osk_oracle_mask_with_skip(tau):
+    w, x = _inputs("tiny_skip")
+    print(f"[case] osk tiny_skip tau={tau}", flush=True)
+    m = okap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
+                                w.q_block, w.page_size, w.budget, w.softmax_scale)
+    n = _run_osk_vs_oracle(w, x, m.blocks, m.counts, tau, f"osk tiny_skip tau={tau}")
+    if 0 <= tau <= 8:
+        assert n > 0
+
+
+def test_osk_any_order_same_output():
+    # reversed and shuffled visiting orders of the same set, skip off
+    w, x = _inputs("tiny", **RAGGED)
+    print("[case] osk any-order", flush=True)
+    blocks, counts = oosk.dense_order_mask(x.cu_seqlens, w.num_q_heads, w.q_block, w.page_size)
+    rng = np.random.default_rng(0)
+    sh = blocks.copy()
+    for idx in np.ndindex(*counts.shape):
+        c = counts[idx]
+        sh[idx][:c] = rng.permutation(sh[idx][:c])
+    _run_osk_vs_oracle(w, x, sh, counts, -1.0, "osk shuffled order")
+
+
+def test_osk_ragged_small_budget_with_kap_order():
+    w, x = _inputs("tiny", **dict(RAGGED, q_dir_gain=6.0))
+    print("[case] osk ragged budget 0.2", flush=True)
+    m = okap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
+                                w.q_block, w.page_size, 0.2, w.softmax_scale)
+    _run_osk_vs_oracle(w, x, m.blocks, m.counts, 2.0, "osk ragged b=0.2 tau=2")
+
+
+def _kap_compare(w, x, budget, label, tiles=None, debug=True):
+    prob, q, k, v = upload(x, DEV)
+    gm = bk.proxy_ordered_mask(prob, q, k, budget, debug=debug)
+    torch.cuda.synchronize()
+    gb, gp, gc, gh = _np(gm.blocks), _np(gm.pages), _np(gm.counts), _np(gm.hrm_counts)
+    beta = okap.budget_ppm(budget)
+    assert gm.capacity == okap.mask_capacity(int(max(w.seqlens)), w.page_size, beta)
+    exact = ties = 0
+    grp = w.num_q_heads // w.num_kv_heads
+    for b in range(w.batch):
+        s0, L = int(x.cu_seqlens[b]), int(x.seqlens[b])
+        nqb = (L + w.q_block - 1) // w.q_block
+        assert np.all(gc[b, :, nqb:] == 0)
+        assert np.all(gb[b, :, nqb:] == -1)
+        if L == 0:
+            continue
+        kk = materialise(x.k_pool, x.page_table[b], L, w.page_size)
+        for h in range(w.num_q_heads):
+            want = None if tiles is None else [i for (bb, hh, i) in tiles if bb == b and hh == h]
+            if want is not None and not want:
+                continue
+            res = okap.head_tiles(x.q[s0:s0 + L, h].astype(np.float64), kk[:, h // grp],
+                                  w.softmax_scale, w.q_block, w.page_size, beta, tiles=want)
+            for i, tile in res.items():
+                kind = check_kap_row(gb[b, h, i], gp[b, h, i], gc[b, h, i], gh[b, h, i], tile,
+                                     x.page_table[b])
+                exact += kind == "exact"
+                ties += kind == "tie"
+    print(f"[parity] {label}: KAP rows exact={exact} near-tie={ties}")
+    return gm, exact, ties
+
+
+@pytest.mark.parametrize("case", [("tiny", {}, 0.5), ("tiny_skip", {}, 0.5),
+                                  ("tiny", dict(RAGGED), 0.3), ("tiny", dict(RAGGED), 1.0),
+                                  ("tiny", dict(RAGGED, q_block=64), 0.05)])
+def test_kap_matches_oracle(case):
+    name, kw, budget = case
+    w, x = _inputs(name, **kw)
+    print(f"[case] kap {name} {kw} budget={budget}", flush=True)
+    _, exact, ties = _kap_compare(w, x, budget, f"kap {name} b={budget}")
+    assert exact > 0 and ties <= max(1, exact // 100)
+
+
+def test_deterministic_and_poison_safe():
+    w, x = _inputs("tiny", **RAGGED)
+    print("[case] determinism", flush=True)
+    prob, q, k, v = upload(x, DEV)
+    outs = []
+    for _ in range(2):
+        m = bk.proxy_ordered_mask(prob, q, k, 0.3)
+        r = bk.osk_prefill(prob, q, k, v, m, 4.0)
+        d = bk.dense_prefill(prob, q, k, v)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (m.blocks, m.pages, m.counts, r.out, r.lse,
+                                          r.skip_record, d.out, d.lse)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    # the pool's spare pages and the tails of last pages hold NaN
+    assert np.isnan(x.k_pool).any()
+    for t in (outs[0][3], outs[0][6]):
+        assert torch.isfinite(t.float()).all()
