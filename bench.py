@@ -48,6 +48,8 @@ def parse():
                     help="also time the workload's budget x tau sweep (extra JSON lines)")
     ap.add_argument("--only", choices=["all", "kap", "osk", "dense"], default="all",
                     help="launch only one kernel kind (for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (traffic-counter scale) and exit")
     return ap.parse_args()
 
 
@@ -57,6 +59,9 @@ def flops_per_slot(q_block: int, head_dim: int, page: int) -> float:
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by KV head with no exchange; see DESIGN.md)", file=sys.stderr)
@@ -228,8 +233,10 @@ def main():
 
 
 def cpu_baseline(w, x, budget, tau, n_tiles):
-    """Time the CPU oracle (KAP + OSK closed form) on a bounded, seeded sample
-    of tiles of the same layer and extrapolate by per-tile work."""
+    """Time the CPU oracle on a bounded sample of the same layer and scale it
+    to the whole layer: the proxy for one full (sequence, head) pair, scaled
+    by the number of query heads, plus the OSK closed form for seeded tiles,
+    scaled by the kept-block count of the layer."""
     from oracle import kap as okap
     from oracle import osk as oosk
     from oracle.paging import materialise
@@ -238,38 +245,61 @@ def cpu_baseline(w, x, budget, tau, n_tiles):
     rng = np.random.default_rng(1234)
     beta = okap.budget_ppm(budget)
     grp = w.num_q_heads // w.num_kv_heads
-    b = int(np.argmax(np.diff(x.cu_seqlens)))
-    s0, L = int(x.cu_seqlens[b]), int(np.diff(x.cu_seqlens)[b])
-    nqb = (L + w.q_block - 1) // w.q_block
+    lens = np.diff(x.cu_seqlens)
+    b = int(np.argmax(lens))
+    s0, L = int(x.cu_seqlens[b]), int(lens[b])
     t_prep = time.perf_counter()
     keys = materialise(x.k_pool, x.page_table[b], L, w.page_size)
     vals = materialise(x.v_pool, x.page_table[b], L, w.page_size)
     prep_s = time.perf_counter() - t_prep
-    tiles = sorted(rng.choice(nqb, size=min(n_tiles, nqb), replace=False).tolist())
-    heads = rng.choice(w.num_q_heads, size=len(tiles)).tolist()
+    h0 = int(rng.integers(w.num_q_heads))
     t0 = time.perf_counter()
-    work_sample = 0.0
-    for i, h in zip(tiles, heads):
-        g = h // grp
-        res = okap.head_tiles(x.q[s0:s0 + L, h].astype(np.float64), keys[:, g], w.softmax_scale,
-                              w.q_block, w.page_size, beta, tiles=[i])[i]
+    tiles = okap.head_tiles(x.q[s0:s0 + L, h0].astype(np.float64), keys[:, h0 // grp],
+                            w.softmax_scale, w.q_block, w.page_size, beta)
+    kap_head_s = time.perf_counter() - t0
+    nqb = len(tiles)
+    pick = sorted(rng.choice(nqb, size=min(n_tiles, nqb), replace=False).tolist())
+    t0 = time.perf_counter()
+    kept_sample = 0
+    for i in pick:
         rows = np.arange(i * w.q_block, min((i + 1) * w.q_block, L))
-        oosk.osk_tile_closed_form(x.q[s0 + rows, h].astype(np.float64), rows, keys[:, g],
-                                  vals[:, g], res.blocks, tau, w.softmax_scale, w.page_size)
-        work_sample += i + 1
-    t_sample = time.perf_counter() - t0
-    # whole-layer work in the same unit (candidate blocks summed over tiles and heads)
-    total_work = 0.0
-    for L_ in np.diff(x.cu_seqlens):
-        n = (int(L_) + w.q_block - 1) // w.q_block
-        total_work += n * (n + 1) / 2
-    total_work *= w.num_q_heads
-    est_ms = (t_sample / work_sample) * total_work * 1e3 + prep_s * 1e3
+        oosk.osk_tile_closed_form(x.q[s0 + rows, h0].astype(np.float64), rows,
+                                  keys[:, h0 // grp], vals[:, h0 // grp], tiles[i].blocks, tau,
+                                  w.softmax_scale, w.page_size)
+        kept_sample += tiles[i].k
+    osk_s = time.perf_counter() - t0
+    # layer totals: proxy work scales with candidate blocks, OSK with kept blocks
+    cand_seq = sum(t.n for t in tiles.values())
+    kept_seq = sum(t.k for t in tiles.values())
+    cand_layer = kept_layer = 0
+    for L_ in lens:
+        n_t = (np.minimum((np.arange((int(L_) + w.q_block - 1) // w.q_block) + 1) * w.q_block,
+                          int(L_)) - 1) // w.page_size + 1
+        cand_layer += int(n_t.sum()) * w.num_q_heads
+        kept_layer += sum(okap.budget_count(int(n), beta) for n in n_t) * w.num_q_heads
+    kap_layer_s = kap_head_s * cand_layer / cand_seq
+    osk_layer_s = osk_s * kept_layer / max(kept_sample, 1)
+    est_ms = (kap_layer_s + osk_layer_s + prep_s * w.batch) * 1e3
     return {"value": round(est_ms, 1), "unit": "ms/layer", "cores": threads, "kind": "oracle",
-            "sample": f"{len(tiles)} seeded (head, tile) pairs of sequence {b} "
-                      f"(KAP score/sort + OSK closed form, fp64 NumPy), "
-                      f"{t_sample:.1f} s, extrapolated by candidate-block count; "
-                      f"includes {prep_s:.1f} s de-paging"}
+            "sample": f"proxy for all {nqb} tiles of one (sequence {b}, head {h0}) pair "
+                      f"({kap_head_s:.1f} s) scaled by candidate blocks; OSK closed form for "
+                      f"{len(pick)} seeded tiles ({osk_s:.1f} s, {kept_sample} kept blocks) "
+                      f"scaled by kept blocks ({kept_layer}); fp64 NumPy; de-paging "
+                      f"{prep_s:.1f} s per sequence; kept-block count of seq {b} {kept_seq}"}
+
+
+def copy_calibration():
+    """Plain 1 GiB device copy, for scaling the HBM traffic counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    c = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        c.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
 if __name__ == "__main__":

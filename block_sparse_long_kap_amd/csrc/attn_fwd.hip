@@ -49,18 +49,23 @@ __device__ __forceinline__ float pair_max(float x) {
 }
 __device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
 
-// K page in LDS: [64 keys][D] bf16, rows padded by 16 bytes so that the
-// 32 rows one MFMA operand read touches fall into distinct banks while every
-// read of a wavefront stays "one base register + immediate offset".
+// K page in LDS: [64 keys][D] bf16 with 16-byte chunks XOR-swizzled by the
+// row, so that the 16-byte operand reads of consecutive key rows land in
+// distinct banks.  Pages are copied HBM -> LDS directly (no registers): lane
+// i of a copy instruction writes the i-th 16-byte slot of its wavefront's
+// span, and fetches whichever logical chunk belongs in that slot.
 template <int D>
 struct KLayout {
-  static constexpr int kStride = D * 2 + 16;
-  static constexpr int kBytes = kPage * kStride;
+  static constexpr int kChunks = D / 8;
+  static constexpr int kSwz = (kChunks < 16 ? kChunks : 16) - 1;
+  static constexpr int kBytes = kPage * D * 2;
   static __device__ __forceinline__ int offset(int row, int chunk16) {
-    return row * kStride + chunk16 * 16;
+    return row * (D * 2) + ((chunk16 ^ (row & kSwz)) << 4);
   }
 };
-// V^T page in LDS: [D][64 keys] bf16, rows padded by 8 bytes (same reason).
+// V^T page in LDS: [D][64 keys] bf16, rows padded by 8 bytes so that the 32
+// rows one operand read touches fall into distinct banks while every read of a
+// wavefront stays "one base register + immediate offset".
 struct VLayout {
   static constexpr int kStride = kPage * 2 + 8;
   static __device__ __forceinline__ int offset(int d, int chunk8) {
@@ -103,11 +108,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   constexpr int BQ = NW * 32;
   constexpr int KCH = D / 8;                         // 16-byte chunks per key row
   constexpr int K_TOTAL = kPage * KCH;               // 16-byte chunks per K page
-  constexpr int K_PER = (K_TOTAL + NT - 1) / NT;
-  constexpr int V_TOTAL = KCH * (kPage / 4);         // (d-chunk, key-quad) pairs
+  static_assert(K_TOTAL % NT == 0, "K page copy must split evenly over the workgroup");
+  constexpr int K_PER = K_TOTAL / NT;
+  constexpr int V_TOTAL = KCH * (kPage / 4);         // (key-quad, d-chunk) pairs
   constexpr int V_PER = (V_TOTAL + NT - 1) / NT;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
+  // Lazy rescaling: the reference max used for the exponentials only moves
+  // when the true running max exceeds it by more than 2^kRescale, so the
+  // accumulator is rarely rescaled; weights stay <= 2^kRescale.
+  constexpr float kRescale = 8.f;
 
   __shared__ __attribute__((aligned(16))) unsigned char sK[2][KLayout<D>::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char sV[2][D * VLayout::kStride];
@@ -136,14 +146,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   }
   const int tile_last = min(tile_q0 + BQ, L) - 1;
   const int cnt = kOrdered ? p.counts[row] : tile_last / kPage + 1;
-  const int32_t* ob = kOrdered ? p.ordered_blocks + row * p.capacity : nullptr;
-  const int32_t* op = kOrdered ? p.ordered_pages + row * p.capacity : nullptr;
-  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
+  // read-only for the whole kernel: lets the uniform slot lookups go
+  // through scalar loads instead of vector loads plus a vmcnt wait
+  const int32_t* __restrict__ ob = kOrdered ? p.ordered_blocks + row * p.capacity : nullptr;
+  const int32_t* __restrict__ op = kOrdered ? p.ordered_pages + row * p.capacity : nullptr;
+  const int32_t* __restrict__ pt = p.page_table + (int64_t)b * p.max_pages;
 
   const int wave_q0 = tile_q0 + wave * 32;
-  const int wave_last = min(wave_q0 + 31, L - 1);     // < wave_q0 if the wave has no rows
+  const int wave_last = min(wave_q0 + 31, L - 1);
   const int qpos = wave_q0 + col;
   const bool row_valid = qpos < L;
+  const bool wave_has_rows = wave_q0 < L;
 
   // ---- Q^T operand (B of S^T = K Q^T), kept in registers for the whole tile
   bf16x8_t qf[KSTEPS];
@@ -157,51 +170,82 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     }
   }
 
-  auto slot_block = [&](int t) -> int { return kOrdered ? ob[t] : t; };
-  auto slot_page = [&](int t) -> int { return kOrdered ? op[t] : pt[t]; };
+  // Slot -> (logical block, page) lookups.  Indices are fetched 64 at a time
+  // into one VGPR (lane l holds slot 64c + l), one chunk ahead, and read out
+  // with v_readlane, so the per-page lookup never waits on memory.
+  const int32_t* __restrict__ page_src = kOrdered ? op : pt;
+  auto load_chunk = [&](const int32_t* src, int c) -> int {
+    const int t = c * 64 + lane;
+    return t < cnt ? src[t] : 0;
+  };
+  int pg_cur = 0, pg_nxt = 0, bl_cur = 0, bl_nxt = 0, chunk = 0;
+  if (cnt > 0) {
+    pg_cur = load_chunk(page_src, 0);
+    pg_nxt = load_chunk(page_src, 1);
+    if (kOrdered) {
+      bl_cur = load_chunk(ob, 0);
+      bl_nxt = load_chunk(ob, 1);
+    }
+  }
+  auto pick = [&](int vc, int vn, int t) -> int {
+    return __builtin_amdgcn_readlane((t >> 6) == chunk ? vc : vn, t & 63);
+  };
+  auto slot_block = [&](int t) -> int { return kOrdered ? pick(bl_cur, bl_nxt, t) : t; };
+  auto slot_page = [&](int t) -> int { return pick(pg_cur, pg_nxt, t); };
+  auto advance_chunks = [&](int t_next) {
+    // called when slot t_next starts a new chunk: rotate and fetch one ahead
+    if ((t_next & 63) == 0 && t_next > 0) {
+      chunk = t_next >> 6;
+      pg_cur = pg_nxt;
+      pg_nxt = load_chunk(page_src, chunk + 1);
+      if (kOrdered) {
+        bl_cur = bl_nxt;
+        bl_nxt = load_chunk(ob, chunk + 1);
+      }
+    }
+  };
+  const int64_t head_stride = (int64_t)kPage * D;              // elements per (page, head)
+  const int64_t page_stride = (int64_t)p.hkv * head_stride;
 
-  u32x4_t kreg[K_PER];
+  // ---- K: HBM -> LDS without registers (16 bytes per lane per instruction)
+  auto copy_k = [&](int page, int buf) {
+    const uint16_t* base = p.k_pool + (int64_t)page * page_stride + (int64_t)g * head_stride;
+#pragma unroll
+    for (int e = 0; e < K_PER; ++e) {
+      const int f = e * NT + tid;              // physical 16-byte slot in the page
+      const int r = f / KCH;
+      const int c = (f % KCH) ^ (r & KLayout<D>::kSwz);
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(base + r * D + c * 8),
+          (__attribute__((address_space(3))) void*)(&sK[buf][(e * NT + wave * 64) * 16]),
+          16, 0, 0);
+    }
+  };
+
+  // ---- V: HBM -> registers -> transposed into LDS.  Pair idx covers keys
+  // 4kq..4kq+3 and dims 8c..8c+7; key-quads vary fastest across lanes so the
+  // transposed LDS writes of 16 lanes fill one V^T row without bank conflicts.
   u32x4_t vreg[V_PER][4];
-
-  auto load_k = [&](int page) {
-    const uint16_t* base = p.k_pool + ((int64_t)page * p.hkv + g) * (kPage * D);
-#pragma unroll
-    for (int e = 0; e < K_PER; ++e) {
-      const int idx = tid + e * NT;
-      if (K_TOTAL % NT == 0 || idx < K_TOTAL) {
-        const int r = idx / KCH, c = idx % KCH;
-        kreg[e] = *reinterpret_cast<const u32x4_t*>(base + r * D + c * 8);
-      }
-    }
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < K_PER; ++e) {
-      const int idx = tid + e * NT;
-      if (K_TOTAL % NT == 0 || idx < K_TOTAL) {
-        const int r = idx / KCH, c = idx % KCH;
-        *reinterpret_cast<u32x4_t*>(&sK[buf][KLayout<D>::offset(r, c)]) = kreg[e];
-      }
-    }
-  };
-  // V: each (d-chunk, key-quad) pair loads 4 keys x 8 dims; keys past the end
-  // of the sequence are replaced by zeros so that unused slots of the last
-  // page (whatever they hold) cannot reach the output through 0 * NaN.
   auto load_v = [&](int page, int block) {
-    const uint16_t* base = p.v_pool + ((int64_t)page * p.hkv + g) * (kPage * D);
+    const uint16_t* base = p.v_pool + (int64_t)page * page_stride + (int64_t)g * head_stride;
+    const bool tail = block * kPage + kPage > L;     // uniform
     const int valid_keys = L - block * kPage;
 #pragma unroll
     for (int e = 0; e < V_PER; ++e) {
       const int idx = tid + e * NT;
       if (V_TOTAL % NT == 0 || idx < V_TOTAL) {
-        const int c = idx % KCH, kq = idx / KCH;
+        const int kq = idx % (kPage / 4), c = idx / (kPage / 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kq * 4 + r;
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(base + key * D + c * 8);
-          const bool ok = key < valid_keys;
+        for (int r = 0; r < 4; ++r)
+          vreg[e][r] = *reinterpret_cast<const u32x4_t*>(base + (kq * 4 + r) * D + c * 8);
+        if (tail) {
+          // unused slots of a sequence's last page may hold anything: zero them
 #pragma unroll
-          for (int w = 0; w < 4; ++w) vreg[e][r][w] = ok ? v[w] : 0u;
+          for (int r = 0; r < 4; ++r) {
+            const bool ok = kq * 4 + r < valid_keys;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) vreg[e][r][w] = ok ? vreg[e][r][w] : 0u;
+          }
         }
       }
     }
@@ -211,17 +255,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     for (int e = 0; e < V_PER; ++e) {
       const int idx = tid + e * NT;
       if (V_TOTAL % NT == 0 || idx < V_TOTAL) {
-        const int c = idx % KCH, kq = idx / KCH;
+        const int kq = idx % (kPage / 4), c = idx / (kPage / 4);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           // dims 2w (low halves) and 2w+1 (high halves) of keys 4kq..4kq+3
           const uint32_t a0 = vreg[e][0][w], a1 = vreg[e][1][w];
           const uint32_t a2 = vreg[e][2][w], a3 = vreg[e][3][w];
           u32x2_t lo, hi;
-          lo[0] = (a0 & 0xFFFFu) | (a1 << 16);
-          lo[1] = (a2 & 0xFFFFu) | (a3 << 16);
-          hi[0] = (a0 >> 16) | (a1 & 0xFFFF0000u);
-          hi[1] = (a2 >> 16) | (a3 & 0xFFFF0000u);
+          lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+          lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+          hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+          hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
           const int d = c * 8 + 2 * w;
           *reinterpret_cast<u32x2_t*>(&sV[buf][VLayout::offset(d, kq)]) = lo;
           *reinterpret_cast<u32x2_t*>(&sV[buf][VLayout::offset(d + 1, kq)]) = hi;
@@ -233,35 +277,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   f32x16_t o[DBLK];
 #pragma unroll
   for (int md = 0; md < DBLK; ++md) o[md] = (f32x16_t){};
-  float m2 = kNegInf;   // running max of this lane's query row, log2 units
-  float lsum = 0.f;     // this lane's half of the running sum
+  float m_true = kNegInf;   // running max of this lane's query row (log2 units)
+  float m_ref = kNegInf;    // reference max of the exponentials (<= m_true)
+  float lsum = 0.f;         // this lane's half of the running sum, relative to m_ref
   int nskip = 0;
   const bool skip_on = kOrdered && p.tau_log2 >= 0.f;
+  const float c2 = p.scale_log2;
 
   int j_cur = 0, j_next = 0;
   if (cnt > 0) {
     j_cur = slot_block(0);
-    load_k(slot_page(0));
-    store_k(0);
+    copy_k(slot_page(0), 0);
     if (cnt > 1) {
       j_next = slot_block(1);
-      load_k(slot_page(1));
+      copy_k(slot_page(1), 1);
     }
     load_v(slot_page(0), j_cur);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   for (int t = 0; t < cnt; ++t) {
+    advance_chunks(t);
     const int buf = t & 1;
     const int key0 = j_cur * kPage;
-    // some key of the page is visible to some valid row of this wave
-    const bool active = wave_q0 < L && key0 <= wave_last;
+    const bool active = wave_has_rows && key0 <= wave_last;
 
-    // ---- S^T = K Q^T for this wave's 32 queries
+    // ---- S^T = K Q^T for this wave's 32 queries (raw dot products)
     f32x16_t s[2];
-    s[0] = (f32x16_t){};
-    s[1] = (f32x16_t){};
-    float bm = kNegInf;
+    float bm = kNegInf;       // block max of this lane's row, log2 units
     if (active) {
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -269,37 +313,40 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
         for (int mb = 0; mb < 2; ++mb) {
           const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
               &sK[buf][KLayout<D>::offset(mb * 32 + col, 2 * ks + hf)]);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                          qf[ks], s[mb], 0, 0, 0);
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, a), qf[ks], ks == 0 ? (f32x16_t){} : s[mb], 0, 0,
+              0);
         }
       }
-      // causal / end-of-sequence mask: key index in the page > lim is masked
-      const bool need_mask = (key0 + kPage - 1 > wave_q0) || (key0 + kPage > L);
-      const int lim = min(qpos, L - 1) - key0 - 4 * hf;
+      if ((key0 + kPage - 1 > wave_q0) || (key0 + kPage > L)) {
+        // causal / end-of-sequence mask (diagonal and tail pages only)
+        const int lim = min(qpos, L - 1) - key0 - 4 * hf;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int koff = mb * 32 + 8 * (r >> 2) + (r & 3);   // compile-time
-          float v = s[mb][r] * p.scale_log2;
-          v = (need_mask && koff > lim) ? kNegInf : v;
-          s[mb][r] = v;
-          bm = fmaxf(bm, v);
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int koff = mb * 32 + 8 * (r >> 2) + (r & 3);
+            s[mb][r] = koff > lim ? kNegInf : s[mb][r];
+          }
       }
-      bm = pair_max(bm);
+      float mx = kNegInf;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+      bm = pair_max(mx) * c2;
     }
 
     // ---- tile-wide vote: every valid row must find the block negligible
     if (skip_on) {
-      const bool pred = !row_valid || (bm < m2 - p.tau_log2);
+      const bool pred = !row_valid || (bm < m_true - p.tau_log2);
       const bool wave_all = __all(pred);
       if (lane == 0) sVote[buf][wave] = wave_all ? 1 : 0;
     }
 
-    // ---- hand the next K page and this V page to LDS; one barrier per page
-    if (t + 1 < cnt) store_k(buf ^ 1);
+    // ---- this V page to LDS; K(t+1) already landed; one barrier per page
     store_v(buf);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     bool skip = false;
@@ -310,42 +357,45 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       skip = all != 0;
     }
 
-    // ---- prefetch K(t+2) and V(t+1) into registers
+    // ---- prefetch: K(t+2) straight into LDS, V(t+1) into registers
     const int j_after = j_next;
     if (t + 2 < cnt) {
       j_next = slot_block(t + 2);
-      load_k(slot_page(t + 2));
+      copy_k(slot_page(t + 2), buf);
     }
     if (t + 1 < cnt) load_v(slot_page(t + 1), j_after);
 
-    if (skip) {
-      ++nskip;
-      if (p.skip_record != nullptr && tid == 0) p.skip_record[row * p.capacity + t] = 1;
-      j_cur = j_after;
-      continue;
+    if (kOrdered) {
+      nskip += skip ? 1 : 0;
+      if (p.skip_record != nullptr && tid == 0) p.skip_record[row * p.capacity + t] = skip ? 1 : 0;
     }
-    if (kOrdered && p.skip_record != nullptr && tid == 0) p.skip_record[row * p.capacity + t] = 0;
 
-    if (active) {
-      // ---- online softmax update (log2 domain)
-      const float mn = fmaxf(m2, bm);
-      const float alpha = (m2 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
-      const float mu = (mn == kNegInf) ? 0.f : mn;
+    if (active && !skip) {
+      // ---- online softmax (log2 domain) with lazy rescaling
+      const float mn = fmaxf(m_true, bm);
+      m_true = mn;
+      const bool need = mn > m_ref + kRescale;
+      if (__any(need)) {
+        const float new_ref = need ? mn : m_ref;
+        const float alpha = (m_ref == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_ref - new_ref);
+        m_ref = new_ref;
+        lsum *= alpha;
+#pragma unroll
+        for (int md = 0; md < DBLK; ++md) o[md] *= alpha;
+      }
+      const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
       float part = 0.f;
       bf16x8_t pb[4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(s[mb][r] - mu);
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[mb][r], c2, -mu));
           part += e;
           pb[mb * 2 + (r >> 3)][r & 7] = (__bf16)e;
         }
       }
-      lsum = alpha * lsum + part;
-      m2 = mn;
-#pragma unroll
-      for (int md = 0; md < DBLK; ++md) o[md] *= alpha;
+      lsum += part;
 
       // ---- O^T += V^T P^T
 #pragma unroll
@@ -393,7 +443,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     }
     if (p.lse != nullptr && hf == 0) {
       p.lse[(int64_t)h * p.total_q + q0 + qpos] =
-          ltot > 0.f ? (m2 + __log2f(ltot)) * kLn2 : kNegInf;
+          ltot > 0.f ? (m_ref + __log2f(ltot)) * kLn2 : kNegInf;
     }
   }
   if (kOrdered && p.row_stats != nullptr && tid == 0) {
