@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tiles", type=int, default=24,
+    ap.add_argument("--cpu-tiles", type=int, default=160,
                     help="oracle sample size (tiles) for the CPU baseline")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the workload's budget x tau sweep (extra JSON lines)")

@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "cosa_internal.h"
 
 namespace cosa {
@@ -73,12 +75,14 @@ struct VLayout {
   }
 };
 
-// Decode the workgroup's (sequence, head, tile): tiles with more causal
-// blocks first; optionally all heads of a KV group on the same XCD.
+// Decode the workgroup's (sequence, head, tile).  Every order launches the
+// tiles with more causal blocks first (longest-processing-time first).
 __device__ __forceinline__ void decode_tile(const AttnParams& p, int bid, int& b, int& h,
                                             int& i) {
   const int hg = p.hq / p.hkv;
-  if (p.xcd_groups > 0) {
+  if (p.order == kOrderXcdGroup) {
+    // consecutive workgroup ids go round-robin over the 8 XCDs: pin each
+    // (sequence, KV head) group to one XCD so its pages stay in that L2
     const int x = bid & 7;
     const int r = bid >> 3;
     const int groups_per_xcd = p.xcd_groups >> 3;
@@ -88,6 +92,19 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, int bid, int& b
     const int gi = rem / hg;
     const int hh = rem - gi * hg;
     const int G = x + 8 * gi;
+    b = G / p.hkv;
+    const int g = G - b * p.hkv;
+    h = g * hg + hh;
+    i = p.nqb - 1 - level;
+  } else if (p.order == kOrderGroupMajor) {
+    // one (sequence, KV head) group at a time over the whole chip, so the
+    // working set is that group's pages (64 MB at 128K) and repeated page
+    // visits across tiles and query heads hit the memory-side cache
+    const int per_group = hg * p.nqb;
+    const int G = bid / per_group;
+    const int r = bid - G * per_group;
+    const int level = r / hg;
+    const int hh = r - level * hg;
     b = G / p.hkv;
     const int g = G - b * p.hkv;
     h = g * hg + hh;
@@ -119,9 +136,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   // accumulator is rarely rescaled; weights stay <= 2^kRescale.
   constexpr float kRescale = 8.f;
 
-  __shared__ __attribute__((aligned(16))) unsigned char sK[2][KLayout<D>::kBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char sV[2][D * VLayout::kStride];
+  // Two buffers per operand as distinct objects: with the buffer index a
+  // compile-time constant in the (2x unrolled) page loop, the compiler can
+  // tell that reads of one buffer do not depend on the asynchronous HBM->LDS
+  // copies into the other, and does not wait for those copies.
+  __shared__ __attribute__((aligned(16))) unsigned char sK0[KLayout<D>::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sK1[KLayout<D>::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sV0[D * VLayout::kStride];
+  __shared__ __attribute__((aligned(16))) unsigned char sV1[D * VLayout::kStride];
   __shared__ int sVote[2][NW];
+  __shared__ int sSlot[2][2][64];   // [page | block][ring chunk][slot]
+  auto kbuf = [&](int buf) -> unsigned char* { return buf ? sK1 : sK0; };
+  auto vbuf_of = [&](int buf) -> unsigned char* { return buf ? sV1 : sV0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -170,37 +196,43 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     }
   }
 
-  // Slot -> (logical block, page) lookups.  Indices are fetched 64 at a time
-  // into one VGPR (lane l holds slot 64c + l), one chunk ahead, and read out
-  // with v_readlane, so the per-page lookup never waits on memory.
+  // Slot -> (logical block, page) lookups come from a two-chunk ring of 64
+  // entries in LDS (uniform-address reads, no vector-memory wait on the page
+  // loop).  Wave 0 fetches chunk c+1 from memory when slot 64c starts and
+  // writes it into the ring one page later, long before it is read.
   const int32_t* __restrict__ page_src = kOrdered ? op : pt;
-  auto load_chunk = [&](const int32_t* src, int c) -> int {
+  auto chunk_entry = [&](const int32_t* src, int c) -> int {
     const int t = c * 64 + lane;
     return t < cnt ? src[t] : 0;
   };
-  int pg_cur = 0, pg_nxt = 0, bl_cur = 0, bl_nxt = 0, chunk = 0;
-  if (cnt > 0) {
-    pg_cur = load_chunk(page_src, 0);
-    pg_nxt = load_chunk(page_src, 1);
-    if (kOrdered) {
-      bl_cur = load_chunk(ob, 0);
-      bl_nxt = load_chunk(ob, 1);
+  if (wave == 0) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      sSlot[0][c][lane] = chunk_entry(page_src, c);
+      if (kOrdered) sSlot[1][c][lane] = chunk_entry(ob, c);
     }
   }
-  auto pick = [&](int vc, int vn, int t) -> int {
-    return __builtin_amdgcn_readlane((t >> 6) == chunk ? vc : vn, t & 63);
+  __syncthreads();   // every wave reads the ring that wave 0 just filled
+  int pend_pg = 0, pend_bl = 0, pend_chunk = -1;
+  auto slot_page = [&](int t) -> int {
+    return __builtin_amdgcn_readfirstlane(sSlot[0][(t >> 6) & 1][t & 63]);
   };
-  auto slot_block = [&](int t) -> int { return kOrdered ? pick(bl_cur, bl_nxt, t) : t; };
-  auto slot_page = [&](int t) -> int { return pick(pg_cur, pg_nxt, t); };
+  auto slot_block = [&](int t) -> int {
+    return kOrdered ? __builtin_amdgcn_readfirstlane(sSlot[1][(t >> 6) & 1][t & 63]) : t;
+  };
   auto advance_chunks = [&](int t_next) {
-    // called when slot t_next starts a new chunk: rotate and fetch one ahead
-    if ((t_next & 63) == 0 && t_next > 0) {
-      chunk = t_next >> 6;
-      pg_cur = pg_nxt;
-      pg_nxt = load_chunk(page_src, chunk + 1);
-      if (kOrdered) {
-        bl_cur = bl_nxt;
-        bl_nxt = load_chunk(ob, chunk + 1);
+    if (pend_chunk >= 0) {   // fetched one page ago: the barrier since has waited for it
+      if (wave == 0) {
+        sSlot[0][pend_chunk & 1][lane] = pend_pg;
+        if (kOrdered) sSlot[1][pend_chunk & 1][lane] = pend_bl;
+      }
+      pend_chunk = -1;
+    }
+    if ((t_next & 63) == 0 && t_next > 0 && ((t_next >> 6) + 1) * 64 < cnt) {
+      pend_chunk = (t_next >> 6) + 1;
+      if (wave == 0) {
+        pend_pg = chunk_entry(page_src, pend_chunk);
+        if (kOrdered) pend_bl = chunk_entry(ob, pend_chunk);
       }
     }
   };
@@ -209,6 +241,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
 
   // ---- K: HBM -> LDS without registers (16 bytes per lane per instruction)
   auto copy_k = [&](int page, int buf) {
+    unsigned char* kb = kbuf(buf);
     const uint16_t* base = p.k_pool + (int64_t)page * page_stride + (int64_t)g * head_stride;
 #pragma unroll
     for (int e = 0; e < K_PER; ++e) {
@@ -217,7 +250,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       const int c = (f % KCH) ^ (r & KLayout<D>::kSwz);
       __builtin_amdgcn_global_load_lds(
           static_cast<const void*>(base + r * D + c * 8),
-          (__attribute__((address_space(3))) void*)(&sK[buf][(e * NT + wave * 64) * 16]),
+          (__attribute__((address_space(3))) void*)(kb + (e * NT + wave * 64) * 16),
           16, 0, 0);
     }
   };
@@ -226,10 +259,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   // 4kq..4kq+3 and dims 8c..8c+7; key-quads vary fastest across lanes so the
   // transposed LDS writes of 16 lanes fill one V^T row without bank conflicts.
   u32x4_t vreg[V_PER][4];
-  auto load_v = [&](int page, int block) {
+  auto load_v = [&](int page) {
     const uint16_t* base = p.v_pool + (int64_t)page * page_stride + (int64_t)g * head_stride;
-    const bool tail = block * kPage + kPage > L;     // uniform
-    const int valid_keys = L - block * kPage;
 #pragma unroll
     for (int e = 0; e < V_PER; ++e) {
       const int idx = tid + e * NT;
@@ -238,6 +269,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           vreg[e][r] = *reinterpret_cast<const u32x4_t*>(base + (kq * 4 + r) * D + c * 8);
+      }
+    }
+  };
+  auto store_v = [&](int buf, int block) {
+    unsigned char* vb = vbuf_of(buf);
+    const bool tail = block * kPage + kPage > L;     // uniform
+    const int valid_keys = L - block * kPage;
+#pragma unroll
+    for (int e = 0; e < V_PER; ++e) {
+      const int idx = tid + e * NT;
+      if (V_TOTAL % NT == 0 || idx < V_TOTAL) {
+        const int kq = idx % (kPage / 4), c = idx / (kPage / 4);
         if (tail) {
           // unused slots of a sequence's last page may hold anything: zero them
 #pragma unroll
@@ -247,15 +290,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
             for (int w = 0; w < 4; ++w) vreg[e][r][w] = ok ? vreg[e][r][w] : 0u;
           }
         }
-      }
-    }
-  };
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < V_PER; ++e) {
-      const int idx = tid + e * NT;
-      if (V_TOTAL % NT == 0 || idx < V_TOTAL) {
-        const int kq = idx % (kPage / 4), c = idx / (kPage / 4);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           // dims 2w (low halves) and 2w+1 (high halves) of keys 4kq..4kq+3
@@ -267,8 +301,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
           hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
           hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
           const int d = c * 8 + 2 * w;
-          *reinterpret_cast<u32x2_t*>(&sV[buf][VLayout::offset(d, kq)]) = lo;
-          *reinterpret_cast<u32x2_t*>(&sV[buf][VLayout::offset(d + 1, kq)]) = hi;
+          *reinterpret_cast<u32x2_t*>(vb + VLayout::offset(d, kq)) = lo;
+          *reinterpret_cast<u32x2_t*>(vb + VLayout::offset(d + 1, kq)) = hi;
         }
       }
     }
@@ -284,6 +318,62 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   const bool skip_on = kOrdered && p.tau_log2 >= 0.f;
   const float c2 = p.scale_log2;
 
+  // ---- logits of one page for this wave's 32 queries (log2 units, masked)
+  // Returns the row's block max; sets `act` to whether any key of the page is
+  // visible to a valid row of the wave (otherwise no MFMA is issued).
+  auto page_logits = [&](int block, int buf, f32x16_t (&sacc)[2], bool& act) {
+    const int key0 = block * kPage;
+    act = wave_has_rows && key0 <= wave_last;
+    if (!act) return;
+    const unsigned char* kb = kbuf(buf);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+            kb + KLayout<D>::offset(mb * 32 + col, 2 * ks + hf));
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, a), qf[ks], ks == 0 ? (f32x16_t){} : sacc[mb], 0, 0,
+            0);
+      }
+    }
+  };
+  auto page_max = [&](int block, f32x16_t (&sacc)[2]) -> float {
+    const int key0 = block * kPage;
+    if ((key0 + kPage - 1 > wave_q0) || (key0 + kPage > L)) {
+      // causal / end-of-sequence mask (diagonal and tail pages only)
+      const int lim = min(qpos, L - 1) - key0 - 4 * hf;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int koff = mb * 32 + 8 * (r >> 2) + (r & 3);
+          sacc[mb][r] = koff > lim ? kNegInf : sacc[mb][r];
+        }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
+    return pair_max(mx) * c2;
+  };
+  auto vote = [&](float bmx, int vbuf) {
+    if (skip_on) {
+      const bool pred = !row_valid || (bmx < m_true - p.tau_log2);
+      const bool wave_all = __all(pred);
+      if (lane == 0) sVote[vbuf][wave] = wave_all ? 1 : 0;
+    }
+  };
+
+  // Software pipeline over the visited pages, one workgroup barrier per page.
+  // Iteration t: read the tile's vote for page t, start the copies of K(t+2)
+  // and V(t+1), issue the MFMAs of S(t+1), then run the softmax of page t
+  // (VALU, overlapping those MFMAs) and its P V product, then mask / reduce
+  // S(t+1) (VALU, overlapping the P V MFMAs) and post the vote for t+1.
+  f32x16_t s_a[2], s_b[2];
+  float bm_c = kNegInf;
+  bool act_c = false;
   int j_cur = 0, j_next = 0;
   if (cnt > 0) {
     j_cur = slot_block(0);
@@ -292,63 +382,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       j_next = slot_block(1);
       copy_k(slot_page(1), 1);
     }
-    load_v(slot_page(0), j_cur);
+    load_v(slot_page(0));
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    page_logits(j_cur, 0, s_a, act_c);
+    if (act_c) bm_c = page_max(j_cur, s_a);
+    vote(bm_c, 0);
+    store_v(0, j_cur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
-  for (int t = 0; t < cnt; ++t) {
-    advance_chunks(t);
-    const int buf = t & 1;
-    const int key0 = j_cur * kPage;
-    const bool active = wave_has_rows && key0 <= wave_last;
-
-    // ---- S^T = K Q^T for this wave's 32 queries (raw dot products)
-    f32x16_t s[2];
-    float bm = kNegInf;       // block max of this lane's row, log2 units
-    if (active) {
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-              &sK[buf][KLayout<D>::offset(mb * 32 + col, 2 * ks + hf)]);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, a), qf[ks], ks == 0 ? (f32x16_t){} : s[mb], 0, 0,
-              0);
-        }
-      }
-      if ((key0 + kPage - 1 > wave_q0) || (key0 + kPage > L)) {
-        // causal / end-of-sequence mask (diagonal and tail pages only)
-        const int lim = min(qpos, L - 1) - key0 - 4 * hf;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int koff = mb * 32 + 8 * (r >> 2) + (r & 3);
-            s[mb][r] = koff > lim ? kNegInf : s[mb][r];
-          }
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-      bm = pair_max(mx) * c2;
-    }
-
-    // ---- tile-wide vote: every valid row must find the block negligible
-    if (skip_on) {
-      const bool pred = !row_valid || (bm < m_true - p.tau_log2);
-      const bool wave_all = __all(pred);
-      if (lane == 0) sVote[buf][wave] = wave_all ? 1 : 0;
-    }
-
-    // ---- this V page to LDS; K(t+1) already landed; one barrier per page
-    store_v(buf);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
+  // one pipeline step; `sc` holds S(t), `sn` receives S(t+1)
+  auto iteration = [&](auto parity, int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
+    advance_chunks(t + 1);   // chunk holding slot t+1 (and t+2) is current
+    constexpr int buf = decltype(parity)::value;   // == t & 1
     bool skip = false;
     if (skip_on) {
       int all = 1;
@@ -356,23 +404,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       for (int w = 0; w < NW; ++w) all &= sVote[buf][w];
       skip = all != 0;
     }
-
-    // ---- prefetch: K(t+2) straight into LDS, V(t+1) into registers
-    const int j_after = j_next;
-    if (t + 2 < cnt) {
-      j_next = slot_block(t + 2);
-      copy_k(slot_page(t + 2), buf);
-    }
-    if (t + 1 < cnt) load_v(slot_page(t + 1), j_after);
-
     if (kOrdered) {
       nskip += skip ? 1 : 0;
       if (p.skip_record != nullptr && tid == 0) p.skip_record[row * p.capacity + t] = skip ? 1 : 0;
     }
 
-    if (active && !skip) {
-      // ---- online softmax (log2 domain) with lazy rescaling
-      const float mn = fmaxf(m_true, bm);
+    // ---- S(t+1): MFMAs in flight while the softmax of page t runs
+    const int j_after = j_next;
+    bool act_n = false;
+    if (t + 1 < cnt) page_logits(j_after, buf ^ 1, sn, act_n);
+
+    // ---- prefetch: K(t+2) straight into LDS, V(t+1) into registers
+    if (t + 2 < cnt) {
+      j_next = slot_block(t + 2);
+      copy_k(slot_page(t + 2), buf);
+    }
+    if (t + 1 < cnt) load_v(slot_page(t + 1));
+    if (act_c && !skip) {
+      // ---- online softmax of page t (log2 domain) with lazy rescaling
+      const float mn = fmaxf(m_true, bm_c);
       m_true = mn;
       const bool need = mn > m_ref + kRescale;
       if (__any(need)) {
@@ -390,7 +440,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[mb][r], c2, -mu));
+          const float e = __builtin_amdgcn_exp2f(fmaf(sc[mb][r], c2, -mu));
           part += e;
           pb[mb * 2 + (r >> 3)][r & 7] = (__bf16)e;
         }
@@ -398,6 +448,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       lsum += part;
 
       // ---- O^T += V^T P^T
+      const unsigned char* vb = vbuf_of(buf);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -405,9 +456,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
           const int d = md * 32 + col;
           u32x4_t a;
           const u32x2_t a0 =
-              *reinterpret_cast<const u32x2_t*>(&sV[buf][VLayout::offset(d, 4 * ks + hf)]);
+              *reinterpret_cast<const u32x2_t*>(vb + VLayout::offset(d, 4 * ks + hf));
           const u32x2_t a1 =
-              *reinterpret_cast<const u32x2_t*>(&sV[buf][VLayout::offset(d, 4 * ks + 2 + hf)]);
+              *reinterpret_cast<const u32x2_t*>(vb + VLayout::offset(d, 4 * ks + 2 + hf));
           a[0] = a0[0];
           a[1] = a0[1];
           a[2] = a1[0];
@@ -417,7 +468,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
         }
       }
     }
+
+    // ---- finish S(t+1): mask, block max, vote; V(t+1) to LDS; one barrier
+    float bm_n = kNegInf;
+    if (t + 1 < cnt) {
+      if (act_n) bm_n = page_max(j_after, sn);
+      vote(bm_n, buf ^ 1);
+      store_v(buf ^ 1, j_after);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    bm_c = bm_n;
+    act_c = act_n;
     j_cur = j_after;
+  };
+  for (int t = 0; t < cnt; t += 2) {
+    iteration(std::integral_constant<int, 0>{}, t, s_a, s_b);
+    if (t + 1 < cnt) iteration(std::integral_constant<int, 1>{}, t + 1, s_b, s_a);
   }
 
   // ---- epilogue: out = O / l, lse = m + ln l

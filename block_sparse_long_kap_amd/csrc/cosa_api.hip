@@ -101,6 +101,11 @@ void fill_attn(cosa::AttnParams& a, const cosa_problem* p, const void* q, const 
   a.max_pages = p->max_pages_per_seq;
   a.nqb = (int32_t)ceil_div(p->max_seqlen, p->q_block);
   a.xcd_groups = xcd_groups(p);
+#ifndef COSA_TILE_ORDER
+#define COSA_TILE_ORDER cosa::kOrderGroupMajor
+#endif
+  a.order = COSA_TILE_ORDER;
+  if (a.order == cosa::kOrderXcdGroup && a.xcd_groups == 0) a.order = cosa::kOrderLevel;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   a.tau_log2 = -1.f;
 }
@@ -141,7 +146,8 @@ COSA_EXPORT int64_t cosa_mask_capacity(const cosa_problem* p, float budget) {
 COSA_EXPORT size_t cosa_kap_workspace_size(const cosa_problem* p) {
   if (validate(p) != COSA_OK) return 0;
   const int64_t n_max = ceil_div(p->max_seqlen, p->kv_block);
-  return (size_t)p->batch * p->num_kv_heads * p->head_dim * n_max * sizeof(float);
+  // pooled keys as a bf16 hi plane and a bf16 lo plane
+  return (size_t)2 * p->batch * p->num_kv_heads * p->head_dim * n_max * sizeof(uint16_t);
 }
 
 COSA_EXPORT cosa_status cosa_check_page_table_host(const cosa_problem* p,
@@ -195,7 +201,7 @@ COSA_EXPORT cosa_status cosa_proxy_ordered_mask(const cosa_problem* p, const voi
   k.k_pool = static_cast<const uint16_t*>(k_pool);
   k.cu_seqlens = p->cu_seqlens;
   k.page_table = p->page_table;
-  k.kbar = static_cast<float*>(workspace);
+  k.kbar = static_cast<uint16_t*>(workspace);
   k.ordered_blocks = ordered_blocks;
   k.ordered_pages = ordered_pages;
   k.counts = counts;

@@ -10,6 +10,14 @@ constexpr int kPage = 64;          // tokens per KV page == logical key block
 constexpr int kProxyRows = 16;     // query rows pooled into one proxy row
 constexpr int kMaxCandidates = 2048;  // KAP: key blocks per tile handled in one pass
 
+// Workgroup -> (sequence, head, tile) orders of the attention kernel.  All
+// of them launch tiles with more causal blocks first.
+enum TileOrder : int32_t {
+  kOrderLevel = 0,      // tile level major, every head of the batch per level
+  kOrderXcdGroup = 1,   // every KV group pinned to one XCD (needs B*Hkv % 8 == 0)
+  kOrderGroupMajor = 2  // one KV group after the other: its K/V stay cache-resident
+};
+
 // Arguments of the attention kernel (dense and ordered-skipping modes).
 struct AttnParams {
   const uint16_t* q;
@@ -27,7 +35,8 @@ struct AttnParams {
   int64_t capacity;
   int64_t total_q;
   int32_t batch, hq, hkv, max_pages, nqb;
-  int32_t xcd_groups;             // >0: B*Hkv, a multiple of 8 -> XCD-affine order
+  int32_t xcd_groups;             // B*Hkv when it is a multiple of 8, else 0
+  int32_t order;                  // tile order, one of TileOrder
   float scale_log2;               // softmax_scale * log2(e)
   float tau_log2;                 // skip threshold * log2(e); < 0 disables
 };
@@ -38,7 +47,7 @@ struct KapParams {
   const uint16_t* k_pool;
   const int32_t* cu_seqlens;
   const int32_t* page_table;
-  float* kbar;                    // workspace fp32 [B][Hkv][D][n_max]
+  uint16_t* kbar;                 // workspace bf16 [hi|lo][B][Hkv][n_max][D]
   int32_t* ordered_blocks;
   int32_t* ordered_pages;
   int32_t* counts;

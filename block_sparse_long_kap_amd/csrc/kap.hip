@@ -7,24 +7,27 @@
 // HRM and non-HRM groups are sorted independently by score, the HRM group is
 // placed first and the leading entries under the stage-1 budget form the
 // ordered mask M_KAP.  §5.1 ("Implementation details") fuses scoring and
-// pooling into one kernel to keep the proxy cheap.  The body of "Block
-// ranking" is not in the text; the score used here is the block-pooled logit
-// (mean query of 16 consecutive rows against the mean key of a page), its
-// per-proxy-row softmax averaged over the tile's proxy rows, and HRM marks
-// the arg-max block of each proxy row.
+// pooling to keep the proxy cheap.  The body of "Block ranking" is not in
+// the text; the score used here is the block-pooled logit (mean query of 16
+// consecutive rows against the mean key of a page), its per-proxy-row softmax
+// averaged over the tile's proxy rows, and HRM marks the arg-max block of
+// each proxy row.
 //
 // Two launches:
-//   kap_pool_keys   one workgroup per (sequence, key block): streams the
-//                   page of every KV head once from HBM and writes the fp32
-//                   mean key, d-major ([d][block]) so the scoring loads of
-//                   neighbouring candidates are contiguous.
-//   kap_select      one workgroup per mask row (sequence, query head, tile):
-//                   pools the tile's queries from HBM into LDS, scores up to
-//                   2048 candidates in registers (fp32 FMA), reduces the
-//                   per-proxy-row max / arg-max / sum with wavefront
-//                   reductions, builds 64-bit sort keys (not HRM, -w, j),
-//                   bitonic-sorts them in LDS and writes the first k block
-//                   ids together with their remapped pages.
+//   kap_pool_keys  one workgroup per (sequence, key block): streams the page
+//                  of every KV head once from HBM and writes the fp32 mean key
+//                  split into bf16 hi + lo halves (x ~= hi + lo to 16 bits).
+//   kap_select     one workgroup per (sequence, query head, 4 consecutive
+//                  tiles): pools the tiles' queries from HBM (4 x 8 proxy rows
+//                  = one 32-row MFMA operand), scores every candidate block
+//                  with v_mfma_f32_32x32x16_bf16 on the split operands
+//                  (hi*hi + hi*lo + lo*hi, fp32-level accuracy), takes
+//                  per-row max / arg-max / sum online in a first pass,
+//                  recomputes the scores for the weights in a second pass,
+//                  builds 64-bit keys (not HRM, -w, j) in LDS, radix-selects
+//                  the k smallest per tile (one wavefront per tile), bitonic-
+//                  sorts only those and writes the first k ids of each tile
+//                  with their remapped pages.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,16 +36,28 @@
 namespace cosa {
 namespace {
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kTilesPerGroup = 4;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// x ~= hi + lo with hi = bf16(x) and lo = bf16(x - hi)
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  const __bf16 h = (__bf16)x;
+  const __bf16 l = (__bf16)(x - (float)h);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, l);
+}
+
 // ---------------------------------------------------------------------------
-// Key pooling: kbar[b][g][d][j] = mean of the valid keys of block j.
+// Key pooling: kbar[plane][b][g][j][d] = mean of the valid keys of block j,
+// plane 0 = bf16 hi, plane 1 = bf16 lo.
 template <int D>
 __global__ __launch_bounds__(256) void kap_pool_keys(const KapParams p) {
   constexpr int NT = 256;
@@ -61,6 +76,7 @@ __global__ __launch_bounds__(256) void kap_pool_keys(const KapParams p) {
   const int c = tid % KCH;
   const int rg = tid / KCH;
   const float inv = 1.f / (float)nvalid;
+  const int64_t plane = (int64_t)p.batch * p.hkv * p.n_max * D;
 
   for (int g = 0; g < p.hkv; ++g) {
     const uint16_t* base = p.k_pool + ((int64_t)page * p.hkv + g) * (kPage * D) + c * 8;
@@ -82,280 +98,451 @@ __global__ __launch_bounds__(256) void kap_pool_keys(const KapParams p) {
       float sum = 0.f;
 #pragma unroll
       for (int k = 0; k < RG; ++k) sum += red[k][tid];
-      p.kbar[(((int64_t)b * p.hkv + g) * D + tid) * p.n_max + j] = sum * inv;
+      uint16_t hi, lo;
+      split_bf16(sum * inv, hi, lo);
+      const int64_t at = (((int64_t)b * p.hkv + g) * p.n_max + j) * D + tid;
+      p.kbar[at] = hi;
+      p.kbar[plane + at] = lo;
     }
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// Wavefront arg-max (ties to the lowest index) and sum.
-__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(v, off);
-    const int oi = __shfl_xor(idx, off);
-    if (ov > v || (ov == v && oi < idx)) {
-      v = ov;
-      idx = oi;
-    }
-  }
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+// Online (max, arg-max, sum of exp2) triples, merged across lanes and waves.
+struct RowStat {
+  float m;   // max score (log2 units)
+  float z;   // sum of exp2(score - m)
+  int a;     // lowest block index reaching m
+};
+__device__ __forceinline__ RowStat merge(RowStat x, RowStat y) {
+  RowStat o;
+  o.m = fmaxf(x.m, y.m);
+  const float ex = x.m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x.m - o.m);
+  const float ey = y.m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(y.m - o.m);
+  o.z = x.z * ex + y.z * ey;
+  o.a = x.m > y.m ? x.a : (y.m > x.m ? y.a : min(x.a, y.a));
+  return o;
 }
 
 template <int D, int R>
-__global__ __launch_bounds__(256) void kap_select(const KapParams p) {
+__global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   constexpr int NT = 256;
   constexpr int NWAVE = NT / 64;
-  constexpr int M = kMaxCandidates / NT;     // candidates per thread
+  constexpr int TPW = kTilesPerGroup;
+  constexpr int MR = TPW * R;                 // proxy rows of the group (16 or 32)
   constexpr int BQ = R * kProxyRows;
-  constexpr int D4 = D / 4;
+  constexpr int KSTEPS = D / 16;
+  constexpr int KCH = D / 8;
+  static_assert(MR <= 32, "one 32-row MFMA operand");
 
-  __shared__ __attribute__((aligned(16))) float sQ[R][D];
-  __shared__ unsigned long long sKey[kMaxCandidates];
-  __shared__ float sRedV[NWAVE][R];
-  __shared__ int sRedI[NWAVE][R];
-  __shared__ float sRowMax[R];
-  __shared__ int sRowArg[R];
-  __shared__ float sRowSum[R];
-  __shared__ int sCount[NWAVE];
+  // 64 KB of sort keys; the pooled queries (2 x 32 x D bf16) live in the
+  // same space before the keys are built
+  __shared__ __attribute__((aligned(16))) unsigned long long sKey[TPW][kMaxCandidates];
+  __shared__ RowStat sStat[NWAVE][32];
+  __shared__ float sRowM[32];
+  __shared__ float sRowInvZ[32];
+  __shared__ int sRowA[32];
+  __shared__ int sHrm[TPW];          // HRM keys per tile
+  __shared__ int sSel[TPW];          // keys kept by the selection
+  __shared__ uint32_t sHist[NWAVE][256];
+  uint16_t* sQhi = reinterpret_cast<uint16_t*>(&sKey[0][0]);
+  uint16_t* sQlo = sQhi + 32 * D;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int hf = lane >> 5;
+  const int col = lane & 31;
 
-  // Same longest-first order as the attention kernel (no XCD affinity needed).
-  const int per_level = p.batch * p.hq;
-  const int level = blockIdx.x / per_level;
-  const int rem = blockIdx.x - level * per_level;
-  const int b = rem / p.hq;
-  const int h = rem - b * p.hq;
-  const int i = p.nqb - 1 - level;
-  const int g = h / (p.hq / p.hkv);
-  const int64_t row = ((int64_t)b * p.hq + h) * p.nqb + i;
+  // One (sequence, KV head) after the other, so that the concurrently running
+  // workgroups share that head's pooled keys (1 MB at 128K) in L2; inside it
+  // the tile groups with the most candidates first, the query heads of the
+  // GQA group side by side.
+  const int ngroups = (p.nqb + TPW - 1) / TPW;
+  const int hg = p.hq / p.hkv;
+  const int per_kv = ngroups * hg;
+  const int G = blockIdx.x / per_kv;
+  const int rem = blockIdx.x - G * per_kv;
+  const int level = rem / hg;
+  const int b = G / p.hkv;
+  const int g = G - b * p.hkv;
+  const int h = g * hg + (rem - level * hg);
+  const int i0 = (ngroups - 1 - level) * TPW;
   const int q0 = p.cu_seqlens[b];
   const int L = p.cu_seqlens[b + 1] - q0;
-  const int tile_q0 = i * BQ;
-  int32_t* ob = p.ordered_blocks + row * p.capacity;
-  int32_t* opg = p.ordered_pages + row * p.capacity;
+  const int nkb = (L + kPage - 1) / kPage;
+  const int32_t* __restrict__ pt = p.page_table + (int64_t)b * p.max_pages;
 
-  if (tile_q0 >= L) {
-    for (int t = tid; t < p.capacity; t += NT) {
-      ob[t] = -1;
-      opg[t] = -1;
+  // per-tile sizes (n = 0 for a tile past the sequence's end)
+  int n_t[TPW], rows_t[TPW];
+  int n_wg = 0;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int i = i0 + t;
+    const bool valid = i < p.nqb && i * BQ < L;
+    n_t[t] = valid ? (min((i + 1) * BQ, L) - 1) / kPage + 1 : 0;
+    rows_t[t] = valid ? min(R, (L - i * BQ + kProxyRows - 1) / kProxyRows) : 0;
+    n_wg = max(n_wg, n_t[t]);
+  }
+  // rows that are past the end of the sequence (or of the group) have no
+  // candidates; cand(m) = number of candidate blocks of proxy row m
+  auto row_cand = [&](int m) -> int {
+    if (m >= MR) return 0;
+    const int start = (i0 + m / R) * BQ + (m % R) * kProxyRows;
+    if (i0 + m / R >= p.nqb || start >= L) return 0;
+    return (min(start + kProxyRows, L) - 1) / kPage + 1;
+  };
+
+  if (n_wg == 0) {
+    for (int t = 0; t < TPW; ++t) {
+      const int i = i0 + t;
+      if (i >= p.nqb) break;
+      const int64_t row = ((int64_t)b * p.hq + h) * p.nqb + i;
+      for (int s = tid; s < p.capacity; s += NT) {
+        p.ordered_blocks[row * p.capacity + s] = -1;
+        p.ordered_pages[row * p.capacity + s] = -1;
+      }
+      if (tid == 0) {
+        p.counts[row] = 0;
+        if (p.hrm_counts != nullptr) p.hrm_counts[row] = 0;
+      }
+      if (p.debug_w != nullptr)
+        for (int jj = tid; jj < p.n_max; jj += NT) p.debug_w[row * p.n_max + jj] = 0.f;
+      if (p.debug_hrm != nullptr)
+        for (int jj = tid; jj < p.n_max; jj += NT) p.debug_hrm[row * p.n_max + jj] = 0;
     }
-    if (tid == 0) {
-      p.counts[row] = 0;
-      if (p.hrm_counts != nullptr) p.hrm_counts[row] = 0;
-    }
-    if (p.debug_w != nullptr)
-      for (int jj = tid; jj < p.n_max; jj += NT) p.debug_w[row * p.n_max + jj] = 0.f;
-    if (p.debug_hrm != nullptr)
-      for (int jj = tid; jj < p.n_max; jj += NT) p.debug_hrm[row * p.n_max + jj] = 0;
     return;
   }
 
-  // ---- proxy rows: mean of 16 consecutive valid queries, pre-scaled
-  for (int idx = tid; idx < R * D4; idx += NT) {
-    const int r = idx / D4, d4 = idx - r * D4;
-    const int a = tile_q0 + r * kProxyRows;
-    const int e = min(a + kProxyRows, L);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int t = a; t < e; ++t) {
-      const u32x2_t v =
-          *reinterpret_cast<const u32x2_t*>(p.q + ((int64_t)(q0 + t) * p.hq + h) * D + 4 * d4);
-      acc[0] += bf16_lo(v[0]);
-      acc[1] += bf16_hi(v[0]);
-      acc[2] += bf16_lo(v[1]);
-      acc[3] += bf16_hi(v[1]);
-    }
-    const float f = e > a ? p.scale / (float)(e - a) : 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) sQ[r][4 * d4 + k] = acc[k] * f;
-  }
-  // per proxy row: last valid position -> candidate count (0 if the row is empty)
-  int rcand[R];
-  int nrows = 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int a = tile_q0 + r * kProxyRows;
-    const int last = min(a + kProxyRows, L) - 1;
-    rcand[r] = a < L ? last / kPage + 1 : 0;
-    nrows += a < L ? 1 : 0;
-  }
-  const int n = (min(tile_q0 + BQ, L) - 1) / kPage + 1;   // tile candidates
-  __syncthreads();
-
-  // ---- scores s[r][j] for the thread's candidates j = tid + NT*m
-  float s[M][R];
-#pragma unroll
-  for (int m = 0; m < M; ++m)
-#pragma unroll
-    for (int r = 0; r < R; ++r) s[m][r] = 0.f;
-  const float* kb = p.kbar + ((int64_t)b * p.hkv + g) * D * p.n_max;
-  for (int d4 = 0; d4 < D4; ++d4) {
-    float qv[R][4];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) qv[r][k] = sQ[r][4 * d4 + k];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const int j = tid + NT * m;
-      if (j < n) {
-        float kv[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) kv[k] = kb[(int64_t)(4 * d4 + k) * p.n_max + j];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) s[m][r] = fmaf(qv[r][k], kv[k], s[m][r]);
-      }
-    }
-  }
-
-  // ---- per proxy row: max and arg-max over its candidates
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float v = kNegInf;
-    int idx = 0x7FFFFFFF;
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const int j = tid + NT * m;
-      if (j < rcand[r] && s[m][r] > v) {   // ascending j per thread: strict > keeps lowest
-        v = s[m][r];
-        idx = j;
-      }
-    }
-    wave_argmax(v, idx);
-    if (lane == 0) {
-      sRedV[wave][r] = v;
-      sRedI[wave][r] = idx;
-    }
-  }
-  __syncthreads();
-  if (tid < R) {
-    float v = sRedV[0][tid];
-    int idx = sRedI[0][tid];
-    for (int w = 1; w < NWAVE; ++w) {
-      const float ov = sRedV[w][tid];
-      const int oi = sRedI[w][tid];
-      if (ov > v || (ov == v && oi < idx)) {
-        v = ov;
-        idx = oi;
-      }
-    }
-    sRowMax[tid] = v;
-    sRowArg[tid] = idx;
-  }
-  __syncthreads();
-
-  // ---- exponentials and per-row sums
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const float mx = sRowMax[r];
-    float part = 0.f;
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const int j = tid + NT * m;
-      const float e = j < rcand[r] ? expf(s[m][r] - mx) : 0.f;
-      s[m][r] = e;
-      part += e;
-    }
-    part = wave_sum(part);
-    if (lane == 0) sRedV[wave][r] = part;
-  }
-  __syncthreads();
-  if (tid < R) {
-    float sum = 0.f;
-    for (int w = 0; w < NWAVE; ++w) sum += sRedV[w][tid];
-    sRowSum[tid] = sum;
-  }
-  __syncthreads();
-
-  // ---- importance, HRM flag and sort key per candidate
-  float inv_sum[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) inv_sum[r] = rcand[r] > 0 ? 1.f / sRowSum[r] : 0.f;
-  const float inv_rows = 1.f / (float)nrows;
-  int my_hrm = 0;
-  int npow = 1;
-  while (npow < n) npow <<= 1;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int j = tid + NT * m;
-    if (j < npow) {
-      unsigned long long key = ~0ull;
-      if (j < n) {
-        float w = 0.f;
-        bool hrm = false;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          w += s[m][r] * inv_sum[r];
-          hrm |= (rcand[r] > 0 && sRowArg[r] == j);
-        }
-        w *= inv_rows;
-        my_hrm += hrm ? 1 : 0;
-        const uint32_t wb = __float_as_uint(w);   // w >= 0: bit order == value order
-        key = ((unsigned long long)(hrm ? 0u : 1u) << 63) |
-              ((unsigned long long)(0x7FFFFFFFu - wb) << 32) | (uint32_t)j;
-        if (p.debug_w != nullptr) p.debug_w[row * p.n_max + j] = w;
-        if (p.debug_hrm != nullptr) p.debug_hrm[row * p.n_max + j] = hrm ? 1 : 0;
-      }
-      sKey[j] = key;
-    }
-  }
-  if (p.debug_w != nullptr)
-    for (int jj = n + tid; jj < p.n_max; jj += NT) p.debug_w[row * p.n_max + jj] = 0.f;
-  if (p.debug_hrm != nullptr)
-    for (int jj = n + tid; jj < p.n_max; jj += NT) p.debug_hrm[row * p.n_max + jj] = 0;
+  // ---- 1) pooled queries (mean of 16 rows, times scale*log2e), split bf16.
+  // Every load of a thread is issued before the first add (no dependent
+  // HBM round trips).
   {
-    int c = my_hrm;
+    constexpr int PAIRS = 32 * KCH / NT;           // (row, 16-byte chunk) pairs per thread
+    static_assert(32 * KCH % NT == 0, "pairs split evenly");
+    const float qscale = p.scale * kLog2e;
+    u32x4_t v[PAIRS][kProxyRows];
+    int nrow[PAIRS];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
-    if (lane == 0) sCount[wave] = c;
+    for (int e = 0; e < PAIRS; ++e) {
+      const int idx = tid + e * NT;
+      const int m = idx / KCH, c = idx % KCH;
+      nrow[e] = 0;
+      int start = 0;
+      if (m < MR && i0 + m / R < p.nqb) {
+        start = (i0 + m / R) * BQ + (m % R) * kProxyRows;
+        nrow[e] = max(min(start + kProxyRows, L) - start, 0);
+      }
+      const uint16_t* src = p.q + ((int64_t)(q0 + start) * p.hq + h) * D + c * 8;
+#pragma unroll
+      for (int t = 0; t < kProxyRows; ++t) {
+        v[e][t] = (u32x4_t){0u, 0u, 0u, 0u};
+        if (t < nrow[e]) v[e][t] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)t * p.hq * D);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < PAIRS; ++e) {
+      const int idx = tid + e * NT;
+      const int m = idx / KCH, c = idx % KCH;
+      float acc[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[x] = 0.f;
+#pragma unroll
+      for (int t = 0; t < kProxyRows; ++t)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          acc[2 * w] += bf16_lo(v[e][t][w]);
+          acc[2 * w + 1] += bf16_hi(v[e][t][w]);
+        }
+      const float f = nrow[e] > 0 ? qscale / (float)nrow[e] : 0.f;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        uint16_t hi, lo;
+        split_bf16(acc[x] * f, hi, lo);
+        sQhi[m * D + c * 8 + x] = hi;
+        sQlo[m * D + c * 8 + x] = lo;
+      }
+    }
   }
   __syncthreads();
 
-  // ---- bitonic sort of npow keys, ascending
-  for (int size = 2; size <= npow; size <<= 1) {
+  // ---- 2) A operand (pooled queries, rows x d) into registers
+  bf16x8_t ahi[KSTEPS], alo[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    ahi[ks] = *reinterpret_cast<const bf16x8_t*>(&sQhi[col * D + ks * 16 + hf * 8]);
+    alo[ks] = *reinterpret_cast<const bf16x8_t*>(&sQlo[col * D + ks * 16 + hf * 8]);
+  }
+  // rows held by this lane's accumulator registers: m = 8(r/4) + 4hf + r%4
+  int cand[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) cand[r] = row_cand(8 * (r >> 2) + 4 * hf + (r & 3));
+
+  const int64_t plane = (int64_t)p.batch * p.hkv * p.n_max * D;
+  const uint16_t* kb_hi = p.kbar + ((int64_t)b * p.hkv + g) * p.n_max * D;
+  const uint16_t* kb_lo = kb_hi + plane;
+  const int nb = (n_wg + 31) / 32;
+
+  // scores of candidate block cb for the 32 rows (log2 units)
+  auto scores = [&](int cb) -> f32x16_t {
+    const int j = min(cb * 32 + col, nkb - 1);   // clamp reads; masked later
+    const uint16_t* bh = kb_hi + (int64_t)j * D + hf * 8;
+    const uint16_t* bl = kb_lo + (int64_t)j * D + hf * 8;
+    f32x16_t acc = {};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const bf16x8_t h8 = *reinterpret_cast<const bf16x8_t*>(bh + ks * 16);
+      const bf16x8_t l8 = *reinterpret_cast<const bf16x8_t*>(bl + ks * 16);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], h8, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], l8, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], h8, acc, 0, 0, 0);
+    }
+    return acc;
+  };
+
+  // ---- 3) pass 1: per-row max, arg-max (lowest block) and sum, online
+  RowStat st[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) st[r] = RowStat{kNegInf, 0.f, 0x7FFFFFFF};
+  for (int cb = wave; cb < nb; cb += NWAVE) {
+    const f32x16_t acc = scores(cb);
+    const int j = cb * 32 + col;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (j < cand[r]) {
+        const float s = acc[r];
+        if (s > st[r].m) {   // blocks arrive in ascending order per lane
+          st[r].z = st[r].z * (st[r].m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(st[r].m - s)) + 1.f;
+          st[r].m = s;
+          st[r].a = j;
+        } else {
+          st[r].z += __builtin_amdgcn_exp2f(s - st[r].m);
+        }
+      }
+    }
+  }
+  // merge over the 32 candidate lanes of each half, then over the waves
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+      RowStat o;
+      o.m = __shfl_xor(st[r].m, off);
+      o.z = __shfl_xor(st[r].z, off);
+      o.a = __shfl_xor(st[r].a, off);
+      st[r] = merge(st[r], o);
+    }
+  }
+  if (col == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sStat[wave][8 * (r >> 2) + 4 * hf + (r & 3)] = st[r];
+  }
+  __syncthreads();
+  if (tid < 32) {
+    RowStat s = sStat[0][tid];
+    for (int w = 1; w < NWAVE; ++w) s = merge(s, sStat[w][tid]);
+    sRowM[tid] = s.m;
+    sRowInvZ[tid] = s.z > 0.f ? 1.f / s.z : 0.f;
+    sRowA[tid] = s.m == kNegInf ? -1 : s.a;
+  }
+  __syncthreads();
+
+  // ---- 4) pass 2: importance w and HRM flag per (tile, candidate) -> keys
+  float rm[16], riz[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = 8 * (r >> 2) + 4 * hf + (r & 3);
+    rm[r] = sRowM[m];
+    riz[r] = sRowInvZ[m];
+  }
+  int npow = 1;
+  while (npow < n_wg) npow <<= 1;
+  if (tid < TPW) sHrm[tid] = 0;
+  __syncthreads();
+
+  auto emit = [&](int t, int j, float wsum) {
+    const int i = i0 + t;
+    unsigned long long key = ~0ull;
+    if (j < n_t[t]) {
+      const float w = wsum / (float)rows_t[t];
+      bool hrm = false;
+#pragma unroll
+      for (int r = 0; r < R; ++r) hrm |= (sRowA[t * R + r] == j);
+      if (hrm) atomicAdd(&sHrm[t], 1);
+      const uint32_t wb = __float_as_uint(w);   // w >= 0: bit order == value order
+      key = ((unsigned long long)(hrm ? 0u : 1u) << 63) |
+            ((unsigned long long)(0x7FFFFFFFu - wb) << 32) | (uint32_t)j;
+      const int64_t row = ((int64_t)b * p.hq + h) * p.nqb + i;
+      if (p.debug_w != nullptr) p.debug_w[row * p.n_max + j] = w;
+      if (p.debug_hrm != nullptr) p.debug_hrm[row * p.n_max + j] = hrm ? 1 : 0;
+    }
+    if (j < npow) sKey[t][j] = key;
+  };
+
+  for (int cb = wave; cb < nb; cb += NWAVE) {
+    const f32x16_t acc = scores(cb);
+    const int j = cb * 32 + col;
+    float part[4];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g4 + e;
+        sum += j < cand[r] ? __builtin_amdgcn_exp2f(acc[r] - rm[r]) * riz[r] : 0.f;
+      }
+      part[g4] = sum;
+    }
+    if (R == 8) {
+      // tile g4 = rows 8g4 .. 8g4+7: four in this lane, four in lane ^ 32
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float w = part[g4] + __shfl_xor(part[g4], 32);
+        if (hf == 0) emit(g4, j, w);
+      }
+    } else {
+      // R == 4: tile 2*g4 + hf = rows 8g4 + 4hf .. +3, all in this lane
+#pragma unroll
+      for (int g4 = 0; g4 < 2; ++g4) emit(2 * g4 + hf, j, part[g4]);
+    }
+  }
+  // padding keys up to the power of two
+  for (int idx = tid; idx < TPW * npow; idx += NT) {
+    const int t = idx / npow, j = idx - (idx / npow) * npow;
+    if (j >= nb * 32) sKey[t][j] = ~0ull;
+  }
+  __syncthreads();
+
+  // ---- 5) top-k selection per tile (wave t handles tile t): radix-select
+  // the k-th smallest key on its upper 32 bits (HRM flag and -w), keep every
+  // key below that value and every key equal to it (ties are broken by the
+  // block index in the sort that follows), compacted in place.
+  static_assert(TPW == NWAVE, "one wave per tile of the group");
+  int k_t[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int n = n_t[t];
+    int k = 0;
+    if (n > 0) {
+      const long long kk = ((long long)n * p.beta_ppm + 999999) / 1000000;
+      k = (int)(kk < 1 ? 1 : (kk > n ? n : kk));
+    }
+    k_t[t] = k;
+  }
+  {
+    const int t = wave;
+    const int n = n_t[t];
+    const int k = k_t[t];
+    int sel = n;                              // keys kept for the final sort
+    if (n > 0 && k < n) {
+      uint32_t prefix = 0, pmask = 0;
+      int need = k;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int bin = lane; bin < 256; bin += 64) sHist[t][bin] = 0;
+        for (int idx = lane; idx < n; idx += 64) {
+          const uint32_t hi = (uint32_t)(sKey[t][idx] >> 32);
+          if ((hi & pmask) == prefix) atomicAdd(&sHist[t][(hi >> shift) & 255u], 1u);
+        }
+        uint32_t c[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[e] = sHist[t][4 * lane + e];
+        const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+        uint32_t incl = mine;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t o = __shfl_up(incl, off);
+          if (lane >= off) incl += o;
+        }
+        uint32_t before = incl - mine;
+        int digit = -1, left = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (digit < 0 && before < (uint32_t)need && before + c[e] >= (uint32_t)need) {
+            digit = 4 * lane + e;
+            left = need - (int)before;
+          }
+          before += c[e];
+        }
+        const unsigned long long found = __ballot(digit >= 0);
+        const int src = __ffsll((long long)found) - 1;
+        digit = __shfl(digit, src);
+        need = __shfl(left, src);
+        prefix |= (uint32_t)digit << shift;
+        pmask |= 0xFFu << shift;
+      }
+      // compact keys with upper half <= prefix to the front, keeping order
+      int written = 0;
+      for (int base = 0; base < n; base += 64) {
+        const int idx = base + lane;
+        const unsigned long long key = idx < n ? sKey[t][idx] : ~0ull;
+        const bool keep = idx < n && (uint32_t)(key >> 32) <= prefix;
+        const unsigned long long bal = __ballot(keep);
+        const int pos = written + __popcll(bal & ((1ull << lane) - 1ull));
+        if (keep) sKey[t][pos] = key;
+        written += __popcll(bal);
+      }
+      sel = written;
+    }
+    if (lane == 0) sSel[t] = sel;
+  }
+  __syncthreads();
+  int npow_sel = 1;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+    while (npow_sel < sSel[t]) npow_sel <<= 1;
+  for (int idx = tid; idx < TPW * npow_sel; idx += NT) {
+    const int t = idx / npow_sel, j = idx - t * npow_sel;
+    if (j >= sSel[t]) sKey[t][j] = ~0ull;
+  }
+  __syncthreads();
+
+  // ---- 6) bitonic sort of the TPW selections together, ascending
+  const int half = npow_sel >> 1;
+  const int lhalf = 31 - __clz(max(half, 1));
+  for (int size = 2; size <= npow_sel; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int pi = tid; pi < (npow >> 1); pi += NT) {
-        const int lo = 2 * stride * (pi / stride) + (pi % stride);
+      for (int pi = tid; pi < TPW * half; pi += NT) {
+        const int t = pi >> lhalf;
+        const int q = pi & (half - 1);
+        const int lo = ((q & ~(stride - 1)) << 1) | (q & (stride - 1));
         const int hi = lo + stride;
         const bool up = (lo & size) == 0;
-        const unsigned long long a = sKey[lo], c = sKey[hi];
+        const unsigned long long a = sKey[t][lo], c = sKey[t][hi];
         if ((a > c) == up) {
-          sKey[lo] = c;
-          sKey[hi] = a;
+          sKey[t][lo] = c;
+          sKey[t][hi] = a;
         }
       }
       __syncthreads();
     }
   }
 
-  // ---- first k entries in order, remapped pages, counts
-  const long long kk = ((long long)n * p.beta_ppm + 999999) / 1000000;
-  const int k = (int)(kk < 1 ? 1 : (kk > n ? n : kk));
-  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
-  for (int t = tid; t < p.capacity; t += NT) {
-    int blk = -1, pg = -1;
-    if (t < k) {
-      blk = (int)(sKey[t] & 0xFFFFFFFFu);
-      pg = pt[blk];
+  // ---- 7) first k entries of every tile, remapped pages, counts
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int i = i0 + t;
+    if (i >= p.nqb) break;
+    const int64_t row = ((int64_t)b * p.hq + h) * p.nqb + i;
+    const int n = n_t[t];
+    const int k = k_t[t];
+    for (int s = tid; s < p.capacity; s += NT) {
+      int blk = -1, pg = -1;
+      if (s < k) {
+        blk = (int)(sKey[t][s] & 0xFFFFFFFFu);
+        pg = pt[blk];
+      }
+      p.ordered_blocks[row * p.capacity + s] = blk;
+      p.ordered_pages[row * p.capacity + s] = pg;
     }
-    ob[t] = blk;
-    opg[t] = pg;
-  }
-  if (tid == 0) {
-    int nh = 0;
-    for (int w = 0; w < NWAVE; ++w) nh += sCount[w];
-    p.counts[row] = k;
-    if (p.hrm_counts != nullptr) p.hrm_counts[row] = nh < k ? nh : k;
+    if (tid == 0) {
+      p.counts[row] = k;
+      if (p.hrm_counts != nullptr) p.hrm_counts[row] = min(k, sHrm[t]);
+    }
+    if (p.debug_w != nullptr)
+      for (int jj = n + tid; jj < p.n_max; jj += NT) p.debug_w[row * p.n_max + jj] = 0.f;
+    if (p.debug_hrm != nullptr)
+      for (int jj = n + tid; jj < p.n_max; jj += NT) p.debug_hrm[row * p.n_max + jj] = 0;
   }
 }
 
@@ -366,7 +553,8 @@ hipError_t launch_kap_t(const KapParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((kap_pool_keys<D>), dim3(nkb, p.batch), dim3(256), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t grid = (int64_t)p.batch * p.hq * p.nqb;
+  const int64_t groups = (p.nqb + kTilesPerGroup - 1) / kTilesPerGroup;
+  const int64_t grid = (int64_t)p.batch * p.hq * groups;
   hipLaunchKernelGGL((kap_select<D, R>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -102,8 +102,10 @@ int64_t cosa_num_q_tiles(const cosa_problem* p);
  * (0, 1].  Returns a negative cosa_status on error. */
 int64_t cosa_mask_capacity(const cosa_problem* p, float budget);
 
-/* Bytes of device workspace cosa_proxy_ordered_mask() needs (pooled keys,
- * fp32 [batch][num_kv_heads][head_dim][n_max]).  0 on an invalid problem. */
+/* Bytes of device workspace cosa_proxy_ordered_mask() needs: the pooled keys
+ * as two bf16 planes (hi, lo) of [batch][num_kv_heads][n_max][head_dim],
+ * i.e. 4 bytes per (sequence, KV head, key block, dim).  0 on an invalid
+ * problem. */
 size_t cosa_kap_workspace_size(const cosa_problem* p);
 
 /* Host-side check of a host copy of cu_seqlens [batch+1] and page_table
