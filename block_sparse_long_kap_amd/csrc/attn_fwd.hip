@@ -318,14 +318,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   const bool skip_on = kOrdered && p.tau_log2 >= 0.f;
   const float c2 = p.scale_log2;
 
-  // ---- logits of one page for this wave's 32 queries (log2 units, masked)
-  // Returns the row's block max; sets `act` to whether any key of the page is
-  // visible to a valid row of the wave (otherwise no MFMA is issued).
-  auto page_logits = [&](int block, int buf, f32x16_t (&sacc)[2], bool& act) {
-    const int key0 = block * kPage;
-    act = wave_has_rows && key0 <= wave_last;
-    if (!act) return;
-    const unsigned char* kb = kbuf(buf);
+  // ---- building blocks of one page step (all straight-line code, so that
+  // the compiler can interleave them inside one basic block)
+  // S^T(page) = K Q^T for this wave's 32 queries: raw dot products
+  auto qk = [&](const unsigned char* kb, f32x16_t (&sacc)[2]) {
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
@@ -338,10 +334,45 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       }
     }
   };
-  auto page_max = [&](int block, f32x16_t (&sacc)[2]) -> float {
+  // P = exp2(S * scale_log2 - mu) rounded to bf16 (the P^T operand), row sum
+  auto softmax_p = [&](const f32x16_t (&sacc)[2], float mu, bf16x8_t (&pb)[4]) -> float {
+    float part = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mb][r], c2, -mu));
+        part += e;
+        pb[mb * 2 + (r >> 3)][r & 7] = (__bf16)e;
+      }
+    }
+    return part;
+  };
+  // O^T += V^T P^T
+  auto pv = [&](const unsigned char* vb, const bf16x8_t (&pb)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int md = 0; md < DBLK; ++md) {
+        const int d = md * 32 + col;
+        u32x4_t a;
+        const u32x2_t a0 = *reinterpret_cast<const u32x2_t*>(vb + VLayout::offset(d, 4 * ks + hf));
+        const u32x2_t a1 =
+            *reinterpret_cast<const u32x2_t*>(vb + VLayout::offset(d, 4 * ks + 2 + hf));
+        a[0] = a0[0];
+        a[1] = a0[1];
+        a[2] = a1[0];
+        a[3] = a1[1];
+        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb[ks],
+                                                        o[md], 0, 0, 0);
+      }
+    }
+  };
+  // causal / end-of-sequence mask (diagonal and tail pages only), then the
+  // row's block max in log2 units
+  auto mask_max = [&](int block, f32x16_t (&sacc)[2]) -> float {
     const int key0 = block * kPage;
     if ((key0 + kPage - 1 > wave_q0) || (key0 + kPage > L)) {
-      // causal / end-of-sequence mask (diagonal and tail pages only)
       const int lim = min(qpos, L - 1) - key0 - 4 * hf;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -366,14 +397,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     }
   };
 
-  // Software pipeline over the visited pages, one workgroup barrier per page.
-  // Iteration t: read the tile's vote for page t, start the copies of K(t+2)
-  // and V(t+1), issue the MFMAs of S(t+1), then run the softmax of page t
-  // (VALU, overlapping those MFMAs) and its P V product, then mask / reduce
-  // S(t+1) (VALU, overlapping the P V MFMAs) and post the vote for t+1.
-  f32x16_t s_a[2], s_b[2];
-  float bm_c = kNegInf;
-  bool act_c = false;
+  // Page loop, one workgroup barrier per visited page.  Iteration t: S(t)
+  // from the K page already in LDS, mask, block max and the tile vote; V(t)
+  // (fetched during the previous page) to LDS; barrier; read the vote; start
+  // the copies of K(t+2) (HBM -> LDS) and V(t+1) (HBM -> registers); then the
+  // softmax and P V of page t unless the tile skips it.
   int j_cur = 0, j_next = 0;
   if (cnt > 0) {
     j_cur = slot_block(0);
@@ -385,18 +413,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     load_v(slot_page(0));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    page_logits(j_cur, 0, s_a, act_c);
-    if (act_c) bm_c = page_max(j_cur, s_a);
-    vote(bm_c, 0);
-    store_v(0, j_cur);
+  }
+  for (int t = 0; t < cnt; ++t) {
+    advance_chunks(t + 1);   // chunk holding slot t+1 (and t+2) is current
+    const int buf = t & 1;
+    const int key0 = j_cur * kPage;
+    // some key of the page is visible to some valid row of this wave
+    const bool active = wave_has_rows && key0 <= wave_last;
+    f32x16_t sacc[2];
+    float bm = kNegInf;
+    if (active) {
+      qk(kbuf(buf), sacc);
+      bm = mask_max(j_cur, sacc);
+    }
+    vote(bm, buf);
+    store_v(buf, j_cur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
 
-  // one pipeline step; `sc` holds S(t), `sn` receives S(t+1)
-  auto iteration = [&](auto parity, int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
-    advance_chunks(t + 1);   // chunk holding slot t+1 (and t+2) is current
-    constexpr int buf = decltype(parity)::value;   // == t & 1
     bool skip = false;
     if (skip_on) {
       int all = 1;
@@ -409,20 +443,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       if (p.skip_record != nullptr && tid == 0) p.skip_record[row * p.capacity + t] = skip ? 1 : 0;
     }
 
-    // ---- S(t+1): MFMAs in flight while the softmax of page t runs
-    const int j_after = j_next;
-    bool act_n = false;
-    if (t + 1 < cnt) page_logits(j_after, buf ^ 1, sn, act_n);
-
     // ---- prefetch: K(t+2) straight into LDS, V(t+1) into registers
+    const int j_after = j_next;
     if (t + 2 < cnt) {
       j_next = slot_block(t + 2);
       copy_k(slot_page(t + 2), buf);
     }
     if (t + 1 < cnt) load_v(slot_page(t + 1));
-    if (act_c && !skip) {
-      // ---- online softmax of page t (log2 domain) with lazy rescaling
-      const float mn = fmaxf(m_true, bm_c);
+
+    if (active && !skip) {
+      // ---- online softmax (log2 domain) with lazy rescaling
+      const float mn = fmaxf(m_true, bm);
       m_true = mn;
       const bool need = mn > m_ref + kRescale;
       if (__any(need)) {
@@ -434,57 +465,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
         for (int md = 0; md < DBLK; ++md) o[md] *= alpha;
       }
       const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
-      float part = 0.f;
       bf16x8_t pb[4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sc[mb][r], c2, -mu));
-          part += e;
-          pb[mb * 2 + (r >> 3)][r & 7] = (__bf16)e;
-        }
-      }
-      lsum += part;
-
-      // ---- O^T += V^T P^T
-      const unsigned char* vb = vbuf_of(buf);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int md = 0; md < DBLK; ++md) {
-          const int d = md * 32 + col;
-          u32x4_t a;
-          const u32x2_t a0 =
-              *reinterpret_cast<const u32x2_t*>(vb + VLayout::offset(d, 4 * ks + hf));
-          const u32x2_t a1 =
-              *reinterpret_cast<const u32x2_t*>(vb + VLayout::offset(d, 4 * ks + 2 + hf));
-          a[0] = a0[0];
-          a[1] = a0[1];
-          a[2] = a1[0];
-          a[3] = a1[1];
-          o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                          pb[ks], o[md], 0, 0, 0);
-        }
-      }
+      lsum += softmax_p(sacc, mu, pb);
+      pv(vbuf_of(buf), pb);
     }
-
-    // ---- finish S(t+1): mask, block max, vote; V(t+1) to LDS; one barrier
-    float bm_n = kNegInf;
-    if (t + 1 < cnt) {
-      if (act_n) bm_n = page_max(j_after, sn);
-      vote(bm_n, buf ^ 1);
-      store_v(buf ^ 1, j_after);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    bm_c = bm_n;
-    act_c = act_n;
     j_cur = j_after;
-  };
-  for (int t = 0; t < cnt; t += 2) {
-    iteration(std::integral_constant<int, 0>{}, t, s_a, s_b);
-    if (t + 1 < cnt) iteration(std::integral_constant<int, 1>{}, t + 1, s_b, s_a);
   }
 
   // ---- epilogue: out = O / l, lse = m + ln l
