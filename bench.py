@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_PROFILE = "profiles/attn_kap_llama128k_hbm_traffic.md"
 
 
 def parse():
@@ -64,11 +65,12 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by KV head with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the path shards by KV head with no exchange)", file=sys.stderr)
         sys.exit(2)
     import torch
 
     import block_sparse_long_kap_amd as bk
+    from block_sparse_long_kap_amd import profsum
     import cosa_inputs as ci
     from block_sparse_long_kap_amd import _lib
 
@@ -156,6 +158,9 @@ def main():
         dense_ms = d0.elapsed_time(d1) / nd
 
     osk_tflops = osk_flops / (osk_ms * 1e-3) / 1e12 if osk_ms > 0 else 0.0
+    # HBM bytes per OSK launch from the committed rocprofv3 counter summary,
+    # only while it was taken on the current kernel sources and settings
+    traffic = profsum.read_traffic(os.path.join(ROOT, TRAFFIC_PROFILE), w.name, budget, tau)
     kap_bytes = (q.numel() * 2 + (w.total_tokens * w.num_kv_heads * w.head_dim * 2)
                  + 2 * mask.blocks.numel() * 4 + mask.counts.numel() * 8)
     result = {
@@ -195,7 +200,10 @@ def main():
         "input_gen_s": round(gen_s, 1),
         "roofline": {"bound": "mfma", "achieved": round(osk_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(osk_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(osk_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                     "traffic_unit": "bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1)",
+                     "traffic_source": None if traffic is None else TRAFFIC_PROFILE,
                      "kernel": "attn_fwd_kernel<128,4,ordered> (cosa_osk_prefill)",
                      "algorithmic_flop_per_launch": osk_flops},
         "cpu_baseline": None,

@@ -20,13 +20,15 @@
 //     from the S^T accumulator registers (rounded to bf16) and the page's V is
 //     staged transposed in LDS, in the key order the accumulator layout
 //     implies.
-//   * K and V^T pages are double-buffered in LDS; the next pages are fetched
-//     into registers while the current one is computed; one workgroup
-//     barrier per visited page carries both the LDS hand-off and the
-//     tile-wide skip vote.
-//   * The tile order is longest-first (tiles with more causal blocks first)
-//     and, when B*Hkv is a multiple of 8, all query heads of one KV head run
-//     on the same XCD so that its K/V pages stay in that XCD's L2.
+//   * K and V^T pages are double-buffered in LDS.  K pages are copied from
+//     HBM straight into LDS two pages ahead; the next V page is loaded into
+//     registers while the current page is computed and transposed into LDS
+//     at the start of the next step.  One workgroup barrier per visited page
+//     carries both the LDS hand-off and the tile-wide skip vote.
+//   * Tile order: one (sequence, KV head) group at a time over the whole
+//     chip, longest tiles (most causal blocks) first inside the group, so the
+//     working set is that group's pages.  A level-major order and one that
+//     pins each group to one XCD are kept as alternatives.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -136,10 +138,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   // accumulator is rarely rescaled; weights stay <= 2^kRescale.
   constexpr float kRescale = 8.f;
 
-  // Two buffers per operand as distinct objects: with the buffer index a
-  // compile-time constant in the (2x unrolled) page loop, the compiler can
-  // tell that reads of one buffer do not depend on the asynchronous HBM->LDS
-  // copies into the other, and does not wait for those copies.
+  // Two buffers per operand as distinct LDS objects, so that the compiler
+  // can tell reads of one buffer from the asynchronous HBM->LDS copies into
+  // the other and does not wait for those copies before the reads.
   __shared__ __attribute__((aligned(16))) unsigned char sK0[KLayout<D>::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char sK1[KLayout<D>::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char sV0[D * VLayout::kStride];

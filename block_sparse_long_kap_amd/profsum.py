@@ -1,0 +1,192 @@
+"""Summarise rocprofv3 CSV output into short text profiles.
+
+Usage (after the rocprofv3 runs named in each mode's docstring)::
+
+    python -m block_sparse_long_kap_amd.profsum stats    KERNEL_STATS.csv  --command "..."
+    python -m block_sparse_long_kap_amd.profsum traffic  FETCH.csv WRITE.csv COPY_FETCH.csv \
+        COPY_WRITE.csv --copy-bytes 1073741824 --workload llama128k --budget 0.1 --tau 8 \
+        --command "..."
+    python -m block_sparse_long_kap_amd.profsum counters COUNTERS.csv --command "..."
+
+Each mode prints Markdown.  The traffic mode also prints one
+``bench-traffic: {json}`` line per attention kernel, which ``bench.py`` reads
+back to fill the roofline's ``traffic`` field, but only while the digest of
+the attention kernel's sources still matches the one recorded with the
+counters (a changed kernel invalidates them).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ATTN_SOURCES = ("csrc/attn_fwd.hip", "csrc/cosa_internal.h", "csrc/cosa_api.hip")
+
+
+def _code_only(text: str) -> str:
+    """Source text without comments and blank space, so that editing a comment
+    does not count as changing the kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def attention_source_digest(read=None) -> str:
+    """sha256 over the code (comments dropped) of the sources that decide what
+    the attention kernel does.  ``read(rel)`` may supply the text of a file."""
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        if read is None:
+            with open(os.path.join(PKG_DIR, rel)) as f:
+                text = f.read()
+        else:
+            text = read(rel)
+        h.update(rel.encode() + b"\0" + _code_only(text).encode() + b"\0")
+    return h.hexdigest()[:16]
+
+
+def short_name(kernel: str) -> str:
+    s = kernel
+    if "::" in s:
+        s = s.split("(anonymous namespace)::")[-1]
+    return re.sub(r"\((cosa::)?\w+Params\)$", "", s)
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def per_kernel_counter(path):
+    """{(kernel, counter): [values per dispatch]} from a counter_collection CSV."""
+    agg = collections.defaultdict(list)
+    for r in _rows(path):
+        agg[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+    return agg
+
+
+def stats_md(path, command):
+    out = ["| kernel | calls | avg ms | min ms | max ms | share |", "|---|---|---|---|---|---|"]
+    for r in _rows(path):
+        out.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | "
+                   f"{float(r['AverageNs']) / 1e6:.4f} | {float(r['MinNs']) / 1e6:.4f} | "
+                   f"{float(r['MaxNs']) / 1e6:.4f} | {float(r['Percentage']):.2f}% |")
+    return "\n".join([f"Command: `{command}`", "", *out])
+
+
+def _copy_kib(path, counter):
+    """Largest per-dispatch value of ``counter`` for the device copy kernel."""
+    best = 0.0
+    for (k, c), v in per_kernel_counter(path).items():
+        if c == counter and "copyBuffer" in k:
+            best = max(best, max(v))
+    if best <= 0:
+        raise SystemExit(f"no copy dispatch with {counter} in {path}")
+    return best
+
+
+def traffic_md(fetch, write, cfetch, cwrite, copy_bytes, workload, budget, tau, command):
+    f_scale = copy_bytes / (_copy_kib(cfetch, "FETCH_SIZE") * 1024.0)
+    w_scale = copy_bytes / (_copy_kib(cwrite, "WRITE_SIZE") * 1024.0)
+    fr, wr = per_kernel_counter(fetch), per_kernel_counter(write)
+    digest = attention_source_digest()
+    lines = [f"Command: `{command}`", "",
+             f"Copy calibration ({copy_bytes} B device copy): FETCH_SIZE x{f_scale:.3f}, "
+             f"WRITE_SIZE x{w_scale:.3f} to reach true bytes.", "",
+             "| kernel | dispatches | FETCH KiB (raw) | WRITE KiB (raw) | read GB (scaled) | "
+             "written GB (scaled) | total GB |", "|---|---|---|---|---|---|---|"]
+    records = []
+    for (k, c), v in sorted(fr.items()):
+        if c != "FETCH_SIZE" or "cosa" not in k:
+            continue
+        wv = wr.get((k, "WRITE_SIZE"))
+        if not wv:
+            continue
+        fk, wk = sum(v) / len(v), sum(wv) / len(wv)
+        rd, wt = fk * 1024 * f_scale, wk * 1024 * w_scale
+        lines.append(f"| `{short_name(k)}` | {len(v)} | {fk:.6g} | {wk:.6g} | {rd / 1e9:.3f} | "
+                     f"{wt / 1e9:.3f} | {(rd + wt) / 1e9:.3f} |")
+        if "attn_fwd_kernel" in k:
+            records.append({"kernel": short_name(k), "workload": workload, "budget": budget,
+                            "tau": tau, "read_bytes": round(rd), "write_bytes": round(wt),
+                            "bytes_per_launch": round(rd + wt), "source_digest": digest})
+    lines.append("")
+    lines += ["bench-traffic: " + json.dumps(r) for r in records]
+    return "\n".join(lines)
+
+
+def counters_md(path, command, xcds=8, simds=1024):
+    agg = per_kernel_counter(path)
+    kernels = sorted({k for k, _ in agg if "cosa" in k})
+    names = sorted({c for _, c in agg})
+    out = [f"Command: `{command}`", "",
+           "| kernel | " + " | ".join(names) + " | MfmaUtil |",
+           "|---|" + "---|" * (len(names) + 1)]
+    for k in kernels:
+        vals = {c: sum(agg[(k, c)]) / len(agg[(k, c)]) for c in names if (k, c) in agg}
+        util = ""
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and vals.get("GRBM_GUI_ACTIVE"):
+            # GRBM_GUI_ACTIVE is summed over the XCDs; busy cycles over the SIMDs
+            util = f"{vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (vals['GRBM_GUI_ACTIVE'] / xcds * simds):.3f}"
+        out.append(f"| `{short_name(k)}` | " +
+                   " | ".join(f"{vals[c]:.4g}" if c in vals else "" for c in names) +
+                   f" | {util} |")
+    return "\n".join(out)
+
+
+def read_traffic(path, workload, budget, tau):
+    """Bytes per launch recorded for the attention kernel with these settings,
+    or None when absent or taken on different kernel sources."""
+    if not os.path.exists(path):
+        return None
+    digest = attention_source_digest()
+    with open(path) as f:
+        for line in f:
+            if not line.startswith("bench-traffic: "):
+                continue
+            r = json.loads(line[len("bench-traffic: "):])
+            if ("true" in r["kernel"] and r["workload"] == workload and
+                    abs(r["budget"] - budget) < 1e-9 and abs(r["tau"] - tau) < 1e-9 and
+                    r["source_digest"] == digest):
+                return r
+    return None
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    sub = ap.add_subparsers(dest="mode", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--command", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch")
+    t.add_argument("write")
+    t.add_argument("copy_fetch")
+    t.add_argument("copy_write")
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--budget", type=float, required=True)
+    t.add_argument("--tau", type=float, required=True)
+    t.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--command", required=True)
+    a = ap.parse_args(argv)
+    if a.mode == "stats":
+        print(stats_md(a.csv, a.command))
+    elif a.mode == "traffic":
+        print(traffic_md(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes, a.workload,
+                         a.budget, a.tau, a.command))
+    else:
+        print(counters_md(a.csv, a.command))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

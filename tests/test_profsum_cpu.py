@@ -1,0 +1,51 @@
+"""Host-only checks of the rocprofv3 summariser that feeds bench.py's traffic field."""
+import csv
+import os
+
+from block_sparse_long_kap_amd import profsum
+
+
+def test_digest_ignores_comments_only():
+    base = {r: f"int x{i} = {i};\n" for i, r in enumerate(profsum.ATTN_SOURCES)}
+    d0 = profsum.attention_source_digest(lambda r: base[r])
+    commented = {r: "// note\n/* block\n comment */" + t + "  // tail\n" for r, t in base.items()}
+    assert profsum.attention_source_digest(lambda r: commented[r]) == d0
+    changed = dict(base)
+    changed[profsum.ATTN_SOURCES[0]] = "int x0 = 7;\n"
+    assert profsum.attention_source_digest(lambda r: changed[r]) != d0
+
+
+def _counter_csv(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writerows(rows)
+
+
+def test_traffic_scaling_and_readback(tmp_path):
+    attn = "void cosa::(anonymous namespace)::attn_fwd_kernel<128, 4, true>(cosa::AttnParams)"
+    _counter_csv(tmp_path / "f.csv", [(attn, "FETCH_SIZE", 100.0), (attn, "FETCH_SIZE", 300.0)])
+    _counter_csv(tmp_path / "w.csv", [(attn, "WRITE_SIZE", 50.0)])
+    _counter_csv(tmp_path / "cf.csv", [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 512.0)])
+    _counter_csv(tmp_path / "cw.csv", [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 1024.0)])
+    md = profsum.traffic_md(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                            str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), 1024 * 1024,
+                            "wl", 0.1, 8.0, "cmd")
+    prof = tmp_path / "p.md"
+    prof.write_text(md)
+    r = profsum.read_traffic(str(prof), "wl", 0.1, 8.0)
+    # fetch: mean 200 KiB x (1 MiB / 512 KiB) = 400 KiB; write: 50 KiB x 1
+    assert r["read_bytes"] == 400 * 1024 and r["write_bytes"] == 50 * 1024
+    assert profsum.read_traffic(str(prof), "wl", 0.2, 8.0) is None
+    assert profsum.read_traffic(str(prof), "other", 0.1, 8.0) is None
+    stale = md.replace(profsum.attention_source_digest(), "0" * 16)
+    prof.write_text(stale)
+    assert profsum.read_traffic(str(prof), "wl", 0.1, 8.0) is None
+
+
+def test_committed_profile_parses():
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    path = os.path.join(root, "profiles", "attn_kap_llama128k_hbm_traffic.md")
+    assert os.path.exists(path)
+    with open(path) as f:
+        assert any(line.startswith("bench-traffic: ") for line in f)
