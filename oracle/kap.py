@@ -32,6 +32,12 @@ the reading taken here:
   ``beta_ppm = floor(beta * 1e6 + 0.5)``; truncation happens after the two
   groups are concatenated, so an HRM block can displace a higher-w non-HRM
   block.
+* Top-p (§5.1 "Hyperparameters", App. D.1: stage-1 Top-p with p = 0.95):
+  the importance scores of a tile sum to 1 (each proxy row's softmax sums to
+  1 over its candidates), so they are read as the probability mass of the
+  blocks; Top-p keeps the shortest prefix of the HRM-first order whose mass
+  reaches p (at least one block; p = 1 keeps every candidate).  Combined
+  with a budget the smaller of the two counts is kept.
 """
 from __future__ import annotations
 
@@ -57,6 +63,21 @@ def budget_count(n: int, beta_ppm: int) -> int:
         return 0
     k = (n * beta_ppm + 999_999) // 1_000_000
     return max(1, min(n, k))
+
+
+def top_p_count(w_in_order: np.ndarray, p: float) -> int:
+    """Smallest k >= 1 whose first k importance scores (in visiting order) add
+    up to at least p; every candidate when p >= 1 or when the sum never gets
+    there."""
+    if not (0.0 < p <= 1.0):
+        raise ValueError("top_p must lie in (0, 1]")
+    n = len(w_in_order)
+    if n == 0:
+        return 0
+    if p >= 1.0:
+        return n
+    reached = np.flatnonzero(np.cumsum(w_in_order) >= p)
+    return int(reached[0]) + 1 if reached.size else n
 
 
 def mask_capacity(max_seqlen: int, kv_block: int, beta_ppm: int) -> int:
@@ -145,22 +166,25 @@ def flag_grouped_order(w: np.ndarray, hrm: np.ndarray) -> np.ndarray:
 
 
 def kap_tile(qbar: np.ndarray, last: np.ndarray, kbar: np.ndarray, scale: float,
-             kv_block: int, beta_ppm: int) -> TileProxy:
+             kv_block: int, beta_ppm: int, top_p=None) -> TileProxy:
     s, p, w, hrm = score_tile(qbar, last, kbar, scale, kv_block)
     order = flag_grouped_order(w, hrm)
     n = len(w)
-    return TileProxy(s, p, w, hrm, order, budget_count(n, beta_ppm), n)
+    k = budget_count(n, beta_ppm)
+    if top_p is not None:
+        k = min(k, top_p_count(w[order], top_p))
+    return TileProxy(s, p, w, hrm, order, k, n)
 
 
 def head_tiles(q_h: np.ndarray, k_g: np.ndarray, scale: float, q_block: int,
                kv_block: int, beta_ppm: int, rows_per_proxy: int = ROWS_PER_PROXY,
-               tiles=None):
+               tiles=None, top_p=None):
     """KAP for every tile (or the listed tiles) of one (sequence, query head)."""
     kbar = pooled_keys(k_g, kv_block)
     qbar, last, valid = pooled_queries(q_h, q_block, rows_per_proxy)
     idx = range(qbar.shape[0]) if tiles is None else tiles
     return {i: kap_tile(qbar[i][valid[i]], last[i][valid[i]], kbar, scale, kv_block,
-                        beta_ppm) for i in idx}
+                        beta_ppm, top_p) for i in idx}
 
 
 @dataclass
@@ -176,11 +200,13 @@ class OrderedMask:
 def proxy_ordered_mask(q: np.ndarray, k_pool: np.ndarray, page_table: np.ndarray,
                        cu_seqlens: np.ndarray, num_kv_heads: int, q_block: int,
                        kv_block: int, budget: float, scale: float,
-                       rows_per_proxy: int = ROWS_PER_PROXY) -> OrderedMask:
+                       rows_per_proxy: int = ROWS_PER_PROXY, top_p=None) -> OrderedMask:
     """M_KAP for a packed batch, in the layout of the C ABI.
 
     q [T][Hq][D], k_pool [P][Hkv][page][D] (bf16-exact values, any float
-    dtype), page_table [B][max_pages], cu_seqlens [B+1].
+    dtype), page_table [B][max_pages], cu_seqlens [B+1].  With ``top_p`` the
+    kept count is the smaller of the budget count and the Top-p count; the
+    capacity stays the budget's.
     """
     T, Hq, D = q.shape
     grp = Hq // num_kv_heads
@@ -205,7 +231,7 @@ def proxy_ordered_mask(q: np.ndarray, k_pool: np.ndarray, page_table: np.ndarray
             g = h // grp
             res = head_tiles(np.asarray(q[start:start + L, h, :], dtype=np.float64),
                              keys[:, g, :], scale, q_block, kv_block, beta_ppm,
-                             rows_per_proxy)
+                             rows_per_proxy, top_p=top_p)
             for i, tp in res.items():
                 kk = tp.k
                 blocks[b, h, i, :kk] = tp.blocks

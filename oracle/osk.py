@@ -23,10 +23,19 @@ disables in-kernel skipping).  A skipped block contributes to neither the
 numerator nor the denominator (only value-side work is removed, §3.3).  The
 comparison is IEEE: -inf < -inf is false, so a row with no key seen yet
 vetoes the skip.  Rows that see no key at all give out = 0, lse = -inf.
+
+Length-adaptive threshold (§5.1 "Hyperparameters", App. D.1: "Delta / N"):
+Delta / N is read as the bound on exp(bm_r - m_r), so a sequence of N tokens
+gets tau = ln(N / Delta) nats.  In that mode the skip is on for every Delta
+> 0, whatever the sign of tau (a sequence shorter than Delta skips every
+block that does not raise some row's max by more than ln(Delta / N)), and
+off for Delta <= 0.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
+from typing import Optional
 
 import numpy as np
 
@@ -56,14 +65,21 @@ def _row_margin(bm, m_prev, tau):
     return np.where(np.isneginf(bm) & ~np.isneginf(m_prev), -np.inf, out)
 
 
+def tau_from_delta(seqlen: int, delta: float) -> float:
+    """tau = ln(N / Delta) nats for a sequence of N tokens (Delta > 0)."""
+    return math.log(seqlen / delta)
+
+
 def osk_tile_sequential(q_rows: np.ndarray, row_pos: np.ndarray, k: np.ndarray,
                         v: np.ndarray, blocks, tau: float, scale: float,
-                        kv_block: int) -> TileResult:
+                        kv_block: int, skip_on: Optional[bool] = None) -> TileResult:
     """Visit ``blocks`` in order with the online softmax and the tile-wide skip.
 
     q_rows [n][D] are the valid query rows of one tile (positions row_pos),
     k, v [L][D] the sequence's keys and values for the matching KV head.
+    ``skip_on`` defaults to ``tau >= 0``.
     """
+    on = tau >= 0 if skip_on is None else skip_on
     n, D = q_rows.shape
     m = np.full(n, -np.inf)
     l = np.zeros(n)
@@ -74,7 +90,7 @@ def osk_tile_sequential(q_rows: np.ndarray, row_pos: np.ndarray, k: np.ndarray,
         bm = s.max(axis=1)
         margin = float(np.max(_row_margin(bm, m, tau))) if n else -np.inf
         margins.append(margin)
-        if tau >= 0 and np.all(bm < m - tau):
+        if on and np.all(bm < m - tau):
             skipped.append(True)
             continue
         skipped.append(False)
@@ -93,7 +109,7 @@ def osk_tile_sequential(q_rows: np.ndarray, row_pos: np.ndarray, k: np.ndarray,
 
 def osk_tile_closed_form(q_rows: np.ndarray, row_pos: np.ndarray, k: np.ndarray,
                          v: np.ndarray, blocks, tau: float, scale: float,
-                         kv_block: int) -> TileResult:
+                         kv_block: int, skip_on: Optional[bool] = None) -> TileResult:
     """The same result without the sequential loop.
 
     A skipped block has bm_r < m_r - tau <= m_r for every row, so skipping never
@@ -103,6 +119,7 @@ def osk_tile_closed_form(q_rows: np.ndarray, row_pos: np.ndarray, k: np.ndarray,
     attention restricted to the keys of the blocks that were not skipped
     (order invariance).
     """
+    on = tau >= 0 if skip_on is None else skip_on
     n = q_rows.shape[0]
     L = k.shape[0]
     blocks = [int(j) for j in blocks]
@@ -112,7 +129,7 @@ def osk_tile_closed_form(q_rows: np.ndarray, row_pos: np.ndarray, k: np.ndarray,
     skipped, margins = [], []
     for t in range(len(blocks)):
         margins.append(float(np.max(_row_margin(bms[t], prev, tau))) if n else -np.inf)
-        skipped.append(tau >= 0 and bool(np.all(bms[t] < prev - tau)))
+        skipped.append(on and bool(np.all(bms[t] < prev - tau)))
         prev = np.maximum(prev, bms[t])
     key_ok = np.zeros(L, dtype=bool)
     for j, sk in zip(blocks, skipped):
@@ -135,11 +152,14 @@ def osk_prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
                 page_table: np.ndarray, cu_seqlens: np.ndarray, num_kv_heads: int,
                 q_block: int, kv_block: int, ordered_blocks: np.ndarray,
                 counts: np.ndarray, tau: float, scale: float,
-                closed_form: bool = False, tiles=None) -> PrefillResult:
+                closed_form: bool = False, tiles=None,
+                delta: Optional[float] = None) -> PrefillResult:
     """OSK over a packed batch given an ordered mask in the C-ABI layout.
 
     ``tiles`` optionally restricts the work to a list of (b, h, i); outputs of
-    other tiles stay zero.
+    other tiles stay zero.  With ``delta`` given, ``tau`` is ignored and each
+    sequence b of length L_b uses tau_b = ln(L_b / delta), the skip being on
+    iff delta > 0.
     """
     T, Hq, D = q.shape
     grp = Hq // num_kv_heads
@@ -157,6 +177,11 @@ def osk_prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
             continue
         if want is not None and not any(t[0] == b for t in want):
             continue
+        if delta is None:
+            tau_b, on = tau, tau >= 0
+        else:
+            on = delta > 0
+            tau_b = tau_from_delta(L, delta) if on else -1.0
         keys = materialise(k_pool, page_table[b], L, page_size)
         vals = materialise(v_pool, page_table[b], L, page_size)
         nqb = (L + q_block - 1) // q_block
@@ -169,7 +194,7 @@ def osk_prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
                 cnt = int(counts[b, h, i])
                 res = fn(np.asarray(q[start + rows, h, :], dtype=np.float64), rows,
                          keys[:, g, :], vals[:, g, :], ordered_blocks[b, h, i, :cnt],
-                         tau, scale, kv_block)
+                         tau_b, scale, kv_block, skip_on=on)
                 out[start + rows, h, :] = res.out
                 lse[h, start + rows] = res.lse
                 rec[b, h, i, :cnt] = res.skipped

@@ -165,3 +165,56 @@ def test_kap_independent_of_page_placement():
     assert np.array_equal(a.blocks, b.blocks)
     assert np.array_equal(b.pages[b.blocks >= 0], perm[b.blocks[b.blocks >= 0]])
     assert np.allclose(materialise(kp, pt[0], 300, 64), materialise(x.k_pool, x.page_table[0], 300, 64))
+
+
+# ---------------------------------------------------------------------------
+# Stage-1 Top-p (CoSA (paperpeel) §5.1 "Hyperparameters", App. D.1)
+
+
+@pytest.mark.parametrize("case", range(9))
+def test_top_p_golden(case):
+    g = _golden()
+    ex_idx, p, cap, want_k, want_blocks = g["top_p"]["cases"][case]
+    ex = g["examples"][ex_idx]
+    q, k = _example_arrays(ex)
+    res = kap.head_tiles(q, k, ex["scale"], ex["q_block"], ex["kv_block"], kap.budget_ppm(cap),
+                         ex["rows_per_proxy"], top_p=p)
+    t = res[0]
+    assert t.k == want_k
+    assert list(t.blocks) == want_blocks
+
+
+def test_top_p_count_hand_values():
+    for w, p, want in _golden()["top_p"]["count_cases"]:
+        assert kap.top_p_count(np.asarray(w), p) == want, (w, p)
+    assert kap.top_p_count(np.zeros(0), 0.5) == 0
+    for bad in (0.0, -0.1, 1.5):
+        with pytest.raises(ValueError):
+            kap.top_p_count(np.ones(3) / 3, bad)
+
+
+def test_top_p_invariants_on_random_tiles():
+    """Kept mass reaches p and the kept prefix minus its last block does not;
+    the count grows with p; p = 1 keeps every candidate."""
+    x = ci.make(ci.get("tiny"))
+    w_ = x.workload
+    L = int(x.cu_seqlens[1])
+    keys = materialise(x.k_pool, x.page_table[0], L, w_.page_size)
+    for h in range(w_.num_q_heads):
+        g = h // (w_.num_q_heads // w_.num_kv_heads)
+        prev = None
+        for p in (0.3, 0.6, 0.9, 0.95, 1.0):
+            tiles = kap.head_tiles(x.q[:L, h, :].astype(np.float64), keys[:, g, :].astype(np.float64),
+                                   w_.softmax_scale, w_.q_block, w_.page_size, kap.budget_ppm(1.0),
+                                   top_p=p)
+            ks = np.array([t.k for t in tiles.values()])
+            for t in tiles.values():
+                mass = math.fsum(t.w[t.order[:t.k]])
+                if p < 1.0:
+                    assert mass >= p and math.fsum(t.w[t.order[:t.k - 1]]) < p
+                else:
+                    assert t.k == t.n
+                assert abs(math.fsum(t.w) - 1.0) < 1e-12
+            if prev is not None:
+                assert np.all(ks >= prev)
+            prev = ks

@@ -76,6 +76,24 @@ MUTATIONS = [
     # OSK: skip threshold with the wrong sign of tau
     (osk, "osk_tile_sequential", "np.all(bm < m - tau)", "np.all(bm < m + tau)",
      [to.test_skip_rule_hand_example]),
+    # Top-p: mass accumulated in plain score order instead of the HRM-first order
+    (kap, "kap_tile", "top_p_count(w[order], top_p)", "top_p_count(np.sort(w)[::-1], top_p)",
+     [lambda: tk.test_top_p_golden(2)]),
+    # Top-p: reaching p exactly not counted as reached
+    (kap, "top_p_count", "np.cumsum(w_in_order) >= p", "np.cumsum(w_in_order) > p",
+     [tk.test_top_p_count_hand_values]),
+    # Top-p: off by one (the block that crosses p left out)
+    (kap, "top_p_count", "int(reached[0]) + 1", "max(int(reached[0]), 1)",
+     [lambda: tk.test_top_p_golden(1), tk.test_top_p_count_hand_values]),
+    # Top-p: budget cap ignored
+    (kap, "kap_tile", "k = min(k, top_p_count(", "k = (0 * k + top_p_count(",
+     [lambda: tk.test_top_p_golden(5)]),
+    # Delta / N: threshold inverted to ln(Delta / N)
+    (osk, "tau_from_delta", "math.log(seqlen / delta)", "math.log(delta / seqlen)",
+     [to.test_tau_from_delta_hand_values]),
+    # Delta / N: skip switched off whenever tau_b comes out negative
+    (osk, "osk_prefill", "on = delta > 0", "on = delta > 0 and tau_from_delta(L, delta) >= 0",
+     [lambda: to.test_delta_mode_negative_tau_still_skips(False)]),
 ]
 
 

@@ -12,7 +12,9 @@
   and the per-row AND ("bucket effect", §3.3 L2.2);
 * tau monotonicity and the three-way block partition (§4.1, Figure 4 text).
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -181,3 +183,61 @@ def test_tau_monotone_and_partition():
                 computed = visited - skipped
                 assert (n - visited) + skipped + computed == n
                 assert visited == m.counts[0, h, i]
+
+
+# ---------------------------------------------------------------------------
+# Length-adaptive threshold Delta / N (CoSA (paperpeel) §5.1, App. D.1)
+
+
+def test_tau_from_delta_hand_values():
+    with open(os.path.join(os.path.dirname(__file__), "golden",
+                           "kap_worked_examples.json")) as f:
+        cases = json.load(f)["delta_threshold"]["cases"]
+    for n, delta, tau in cases:
+        assert abs(osk.tau_from_delta(n, delta) - tau) < 1e-6
+
+
+def _two_block_sequence():
+    """L = 4, page 2, D = 1, q = 1, keys (1, 1 | 0.5, 0.5), values (1, 1 | 3, 3),
+    identity pages, one 4-row tile visiting [0, 1]."""
+    q = np.ones((4, 1, 1))
+    k_pool = np.array([1.0, 1.0, 0.5, 0.5]).reshape(2, 1, 2, 1)
+    v_pool = np.array([1.0, 1.0, 3.0, 3.0]).reshape(2, 1, 2, 1)
+    pt = np.array([[0, 1]])
+    cu = np.array([0, 4])
+    blocks = np.array([0, 1], dtype=np.int32).reshape(1, 1, 1, 2)
+    counts = np.array([2], dtype=np.int32).reshape(1, 1, 1)
+    return q, k_pool, v_pool, pt, cu, blocks, counts
+
+
+@pytest.mark.parametrize("closed", [False, True])
+def test_delta_mode_negative_tau_still_skips(closed):
+    """With N = 4 and Delta = 4e, tau = ln(N / Delta) = -1 < 0: in the Delta / N
+    mode the skip stays on.  After block 0 every row has m = 1; block 1 has
+    bm = 0.5 for rows 2-3 (0.5 < 1 + 1) and -inf for rows 0-1, so the tile
+    skips it and rows 2-3 average block 0's values only (out = 1).  With the
+    plain tau = -1 (skip off) row 2 (keys 0-2) gets (2e*1 + e^0.5*3) / (2e + e^0.5)
+    and row 3 (keys 0-3) gets (2e*1 + 2e^0.5*3) / (2e + 2e^0.5)."""
+    q, kp, vp, pt, cu, blocks, counts = _two_block_sequence()
+    on = osk.osk_prefill(q, kp, vp, pt, cu, 1, 4, 2, blocks, counts, tau=0.0, scale=1.0,
+                         closed_form=closed, delta=4 * math.e)
+    assert on.skip_record[0, 0, 0].tolist() == [0, 1]
+    assert np.allclose(on.out[:, 0, 0], 1.0, atol=1e-15)
+    off = osk.osk_prefill(q, kp, vp, pt, cu, 1, 4, 2, blocks, counts, tau=-1.0, scale=1.0,
+                          closed_form=closed)
+    assert off.skip_record[0, 0, 0].tolist() == [0, 0]
+    e, h = math.e, math.exp(0.5)
+    want = [(2 * e + h * 3) / (2 * e + h), (2 * e + 2 * h * 3) / (2 * e + 2 * h)]
+    assert np.allclose(off.out[2:, 0, 0], want, atol=1e-14)
+    assert np.allclose(off.out[:2, 0, 0], 1.0, atol=1e-15)
+    # Delta <= 0 switches the skip off in the Delta / N mode as well
+    neg = osk.osk_prefill(q, kp, vp, pt, cu, 1, 4, 2, blocks, counts, tau=5.0, scale=1.0,
+                          closed_form=closed, delta=-1.0)
+    assert neg.skip_record[0, 0, 0].tolist() == [0, 0]
+    # tau_b = ln(4 / Delta) = 0.6 > bm-margin: 0.5 < 1 - 0.6 is false, computed
+    mid = osk.osk_prefill(q, kp, vp, pt, cu, 1, 4, 2, blocks, counts, tau=0.0, scale=1.0,
+                          closed_form=closed, delta=4 * math.exp(-0.6))
+    assert mid.skip_record[0, 0, 0].tolist() == [0, 0]
+    lo = osk.osk_prefill(q, kp, vp, pt, cu, 1, 4, 2, blocks, counts, tau=0.0, scale=1.0,
+                         closed_form=closed, delta=4 * math.exp(-0.4))
+    assert lo.skip_record[0, 0, 0].tolist() == [0, 1]
