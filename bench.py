@@ -31,6 +31,9 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_PROFILE = "profiles/attn_kap_llama128k_hbm_traffic.md"
+# (Top-p, Delta) operating points of the pages: Qwen3-8B uses p = 0.95 with
+# Delta = 2000 (1000 for the accuracy-first variant), Llama-3.1-8B Delta = 200
+TOP_P_DELTA_POINTS = [(0.95, 2000.0), (0.95, 1000.0), (0.95, 200.0), (0.9, 200.0)]
 
 
 def parse():
@@ -46,7 +49,8 @@ def parse():
     ap.add_argument("--cpu-tiles", type=int, default=160,
                     help="oracle sample size (tiles) for the CPU baseline")
     ap.add_argument("--sweep", action="store_true",
-                    help="also time the workload's budget x tau sweep (extra JSON lines)")
+                    help="also time the workload's budget x tau sweep and the Top-p / Delta "
+                         "operating points (extra JSON lines)")
     ap.add_argument("--only", choices=["all", "kap", "osk", "dense"], default="all",
                     help="launch only one kernel kind (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -238,6 +242,35 @@ def main():
                                   "stage1_budget": round(vis / causal_slots, 5),
                                   "skip_ratio": round(skp / max(vis, 1), 5),
                                   "osk_tflops": round(fl / om / 1e9, 1)}), flush=True)
+        # the pages' own knobs: stage-1 Top-p (no budget cap) with the
+        # length-adaptive threshold ln(N / Delta)
+        for p_, d_ in TOP_P_DELTA_POINTS:
+            m2 = bk.proxy_ordered_mask_top_p(prob, q, kp, p_, 1.0, workspace=ws)
+            r2 = bk.osk_prefill_delta(prob, q, kp, vp, m2, d_, record=True)
+            torch.cuda.synchronize()
+            st = r2.row_stats.cpu().numpy().reshape(-1, 2)
+            e0, e1, e2 = ev(), ev(), ev()
+            e0.record(stream)
+            for _ in range(args.steps):
+                bk.proxy_ordered_mask_top_p(prob, q, kp, p_, 1.0, workspace=ws, out=m2)
+            e1.record(stream)
+            for _ in range(args.steps):
+                bk.osk_prefill_delta(prob, q, kp, vp, m2, d_, out=out)
+            e2.record(stream)
+            torch.cuda.synchronize()
+            km, om = e0.elapsed_time(e1) / args.steps, e1.elapsed_time(e2) / args.steps
+            vis, skp = int(st[:, 0].sum()), int(st[:, 1].sum())
+            fl = fps * (2 * vis - skp)
+            print(json.dumps({"sweep": w.name, "top_p": p_, "delta": d_,
+                              "tau_at_max_len": round(float(np.log(w.max_seqlen / d_)), 4),
+                              "kap_ms": round(km, 4), "osk_ms": round(om, 4),
+                              "ms_per_layer": round(km + om, 4),
+                              "speedup_vs_dense": None if dense_ms is None else
+                              round(dense_ms / (km + om), 3),
+                              "stage1_budget": round(vis / causal_slots, 5),
+                              "skip_ratio": round(skp / max(vis, 1), 5),
+                              "effective_budget": round((vis - skp) / causal_slots, 5),
+                              "osk_tflops": round(fl / om / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(w, x, budget, tau, n_tiles):

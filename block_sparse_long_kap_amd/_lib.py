@@ -56,8 +56,12 @@ SIGNATURES = {
     "cosa_check_page_table_host": (c_i32, [P, c_vp, c_vp]),
     "cosa_proxy_ordered_mask": (c_i32, [P, c_vp, c_vp, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                         c_i64, c_vp, c_size, c_vp]),
+    "cosa_proxy_ordered_mask_top_p": (c_i32, [P, c_vp, c_vp, c_f32, c_f32, c_vp, c_vp, c_vp,
+                                              c_vp, c_vp, c_vp, c_i64, c_vp, c_size, c_vp]),
     "cosa_osk_prefill": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_f32, c_vp, c_vp,
                                  c_vp, c_vp, c_vp]),
+    "cosa_osk_prefill_delta": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_f32, c_vp,
+                                       c_vp, c_vp, c_vp, c_vp]),
     "cosa_dense_prefill": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
 }
 

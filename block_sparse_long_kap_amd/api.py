@@ -143,12 +143,7 @@ class KapWorkspace:
         self.buf = torch.empty(max(self.nbytes, 1), dtype=torch.uint8, device=problem.device)
 
 
-def proxy_ordered_mask(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor, budget: float,
-                       *, capacity: Optional[int] = None, hrm_counts: bool = True,
-                       debug: bool = False, workspace: Optional[KapWorkspace] = None,
-                       out: Optional[OrderedMask] = None) -> OrderedMask:
-    """KAP ordered mask (``cosa_proxy_ordered_mask``)."""
-    lib = _lib.load()
+def _mask_buffers(problem: Problem, q, k_pool, budget, capacity, hrm_counts, debug, out):
     problem._check_qkv(q, k_pool)
     dev = problem.device
     C = problem.mask_capacity(budget) if capacity is None else int(capacity)
@@ -165,12 +160,41 @@ def proxy_ordered_mask(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor, 
             n_max = -(-problem.max_seqlen // problem.page_size)
             out.debug_w = torch.empty(rows + (n_max,), dtype=torch.float32, device=dev)
             out.debug_hrm = torch.empty(rows + (n_max,), dtype=torch.uint8, device=dev)
+    return out
+
+
+def proxy_ordered_mask(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor, budget: float,
+                       *, capacity: Optional[int] = None, hrm_counts: bool = True,
+                       debug: bool = False, workspace: Optional[KapWorkspace] = None,
+                       out: Optional[OrderedMask] = None) -> OrderedMask:
+    """KAP ordered mask (``cosa_proxy_ordered_mask``)."""
+    lib = _lib.load()
+    out = _mask_buffers(problem, q, k_pool, budget, capacity, hrm_counts, debug, out)
     ws = workspace if workspace is not None else KapWorkspace(problem)
     st = lib.cosa_proxy_ordered_mask(
         problem.ref(), _ptr(q), _ptr(k_pool), ctypes.c_float(budget), _ptr(out.blocks),
         _ptr(out.pages), _ptr(out.counts), _ptr(out.hrm_counts), _ptr(out.debug_w),
-        _ptr(out.debug_hrm), out.capacity, _ptr(ws.buf), ws.nbytes, _stream(dev))
+        _ptr(out.debug_hrm), out.capacity, _ptr(ws.buf), ws.nbytes, _stream(problem.device))
     _lib.check(st, "cosa_proxy_ordered_mask")
+    return out
+
+
+def proxy_ordered_mask_top_p(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor,
+                             top_p: float, budget: float = 1.0, *,
+                             capacity: Optional[int] = None, hrm_counts: bool = True,
+                             debug: bool = False, workspace: Optional[KapWorkspace] = None,
+                             out: Optional[OrderedMask] = None) -> OrderedMask:
+    """KAP ordered mask with stage-1 Top-p under a budget cap
+    (``cosa_proxy_ordered_mask_top_p``)."""
+    lib = _lib.load()
+    out = _mask_buffers(problem, q, k_pool, budget, capacity, hrm_counts, debug, out)
+    ws = workspace if workspace is not None else KapWorkspace(problem)
+    st = lib.cosa_proxy_ordered_mask_top_p(
+        problem.ref(), _ptr(q), _ptr(k_pool), ctypes.c_float(top_p), ctypes.c_float(budget),
+        _ptr(out.blocks), _ptr(out.pages), _ptr(out.counts), _ptr(out.hrm_counts),
+        _ptr(out.debug_w), _ptr(out.debug_hrm), out.capacity, _ptr(ws.buf), ws.nbytes,
+        _stream(problem.device))
+    _lib.check(st, "cosa_proxy_ordered_mask_top_p")
     return out
 
 
@@ -182,11 +206,7 @@ class PrefillOutput:
     row_stats: Optional[torch.Tensor] = None     # int32 [B][Hq][NQB][2]
 
 
-def osk_prefill(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
-                mask: OrderedMask, skip_tau: float, *, lse: bool = True, record: bool = True,
-                out: Optional[PrefillOutput] = None) -> PrefillOutput:
-    """Ordered-Skipping Kernel (``cosa_osk_prefill``); skip_tau < 0 disables the skip."""
-    lib = _lib.load()
+def _prefill_buffers(problem: Problem, q, k_pool, v_pool, mask, lse, record, out):
     problem._check_qkv(q, k_pool, v_pool)
     dev = problem.device
     nqb = problem.num_q_tiles()
@@ -202,12 +222,38 @@ def osk_prefill(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor, v_pool:
             skip_record=torch.zeros(rows + (mask.capacity,), dtype=torch.uint8, device=dev)
             if record else None,
             row_stats=torch.zeros(rows + (2,), dtype=torch.int32, device=dev) if record else None)
+    return out
+
+
+def osk_prefill(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                mask: OrderedMask, skip_tau: float, *, lse: bool = True, record: bool = True,
+                out: Optional[PrefillOutput] = None) -> PrefillOutput:
+    """Ordered-Skipping Kernel (``cosa_osk_prefill``); skip_tau < 0 disables the skip."""
+    lib = _lib.load()
+    out = _prefill_buffers(problem, q, k_pool, v_pool, mask, lse, record, out)
     st = lib.cosa_osk_prefill(problem.ref(), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                               _ptr(mask.blocks), _ptr(mask.pages), _ptr(mask.counts),
                               mask.capacity, ctypes.c_float(skip_tau), _ptr(out.out),
                               _ptr(out.lse), _ptr(out.skip_record), _ptr(out.row_stats),
-                              _stream(dev))
+                              _stream(problem.device))
     _lib.check(st, "cosa_osk_prefill")
+    return out
+
+
+def osk_prefill_delta(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor,
+                      v_pool: torch.Tensor, mask: OrderedMask, skip_delta: float, *,
+                      lse: bool = True, record: bool = True,
+                      out: Optional[PrefillOutput] = None) -> PrefillOutput:
+    """Ordered-Skipping Kernel with the per-sequence threshold ln(L_b / Delta)
+    (``cosa_osk_prefill_delta``); skip_delta <= 0 disables the skip."""
+    lib = _lib.load()
+    out = _prefill_buffers(problem, q, k_pool, v_pool, mask, lse, record, out)
+    st = lib.cosa_osk_prefill_delta(problem.ref(), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                    _ptr(mask.blocks), _ptr(mask.pages), _ptr(mask.counts),
+                                    mask.capacity, ctypes.c_float(skip_delta), _ptr(out.out),
+                                    _ptr(out.lse), _ptr(out.skip_record), _ptr(out.row_stats),
+                                    _stream(problem.device))
+    _lib.check(st, "cosa_osk_prefill_delta")
     return out
 
 

@@ -316,7 +316,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   float m_ref = kNegInf;    // reference max of the exponentials (<= m_true)
   float lsum = 0.f;         // this lane's half of the running sum, relative to m_ref
   int nskip = 0;
-  const bool skip_on = kOrdered && p.tau_log2 >= 0.f;
+  const bool skip_on = kOrdered && p.skip_mode != kSkipOff;
+  // threshold in log2 units: fixed, or log2(L / Delta) for this sequence
+  const float tau_l2 = p.skip_mode == kSkipDelta ? __log2f((float)L) - p.log2_delta : p.tau_log2;
   const float c2 = p.scale_log2;
 
   // ---- building blocks of one page step (all straight-line code, so that
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   };
   auto vote = [&](float bmx, int vbuf) {
     if (skip_on) {
-      const bool pred = !row_valid || (bmx < m_true - p.tau_log2);
+      const bool pred = !row_valid || (bmx < m_true - tau_l2);
       const bool wave_all = __all(pred);
       if (lane == 0) sVote[vbuf][wave] = wave_all ? 1 : 0;
     }

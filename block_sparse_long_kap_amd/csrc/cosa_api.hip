@@ -107,7 +107,9 @@ void fill_attn(cosa::AttnParams& a, const cosa_problem* p, const void* q, const 
   a.order = COSA_TILE_ORDER;
   if (a.order == cosa::kOrderXcdGroup && a.xcd_groups == 0) a.order = cosa::kOrderLevel;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  a.tau_log2 = -1.f;
+  a.skip_mode = cosa::kSkipOff;
+  a.tau_log2 = 0.f;
+  a.log2_delta = 0.f;
 }
 
 }  // namespace
@@ -174,13 +176,12 @@ COSA_EXPORT cosa_status cosa_check_page_table_host(const cosa_problem* p,
   return ok();
 }
 
-COSA_EXPORT cosa_status cosa_proxy_ordered_mask(const cosa_problem* p, const void* q,
-                                                const void* k_pool, float budget,
-                                                int32_t* ordered_blocks, int32_t* ordered_pages,
-                                                int32_t* counts, int32_t* hrm_counts,
-                                                float* debug_w, uint8_t* debug_hrm,
-                                                int64_t capacity, void* workspace,
-                                                size_t workspace_bytes, void* stream) {
+namespace {
+
+cosa_status proxy_mask(const cosa_problem* p, const void* q, const void* k_pool, float budget,
+                       uint64_t top_p_fx, int32_t* ordered_blocks, int32_t* ordered_pages,
+                       int32_t* counts, int32_t* hrm_counts, float* debug_w, uint8_t* debug_hrm,
+                       int64_t capacity, void* workspace, size_t workspace_bytes, void* stream) {
   cosa_status st = validate(p);
   if (st != COSA_OK) return st;
   if (q == nullptr || k_pool == nullptr || ordered_blocks == nullptr ||
@@ -217,7 +218,33 @@ COSA_EXPORT cosa_status cosa_proxy_ordered_mask(const cosa_problem* p, const voi
   k.n_max = (int32_t)n_max;
   k.beta_ppm = ppm;
   k.scale = p->softmax_scale;
+  k.top_p_fx = top_p_fx;
   return hip_status(cosa::launch_kap(k, p->head_dim, p->q_block, (hipStream_t)stream));
+}
+
+}  // namespace
+
+COSA_EXPORT cosa_status cosa_proxy_ordered_mask(const cosa_problem* p, const void* q,
+                                                const void* k_pool, float budget,
+                                                int32_t* ordered_blocks, int32_t* ordered_pages,
+                                                int32_t* counts, int32_t* hrm_counts,
+                                                float* debug_w, uint8_t* debug_hrm,
+                                                int64_t capacity, void* workspace,
+                                                size_t workspace_bytes, void* stream) {
+  return proxy_mask(p, q, k_pool, budget, 0, ordered_blocks, ordered_pages, counts, hrm_counts,
+                    debug_w, debug_hrm, capacity, workspace, workspace_bytes, stream);
+}
+
+COSA_EXPORT cosa_status cosa_proxy_ordered_mask_top_p(
+    const cosa_problem* p, const void* q, const void* k_pool, float top_p, float budget,
+    int32_t* ordered_blocks, int32_t* ordered_pages, int32_t* counts, int32_t* hrm_counts,
+    float* debug_w, uint8_t* debug_hrm, int64_t capacity, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (!(top_p > 0.f) || !(top_p <= 1.f)) return fail(COSA_ERR_INVALID_ARG, "top_p must lie in (0, 1]");
+  // p * 2^48 rounded down (exact in double); p = 1 keeps every candidate
+  const uint64_t fx = top_p >= 1.f ? ~0ull : (uint64_t)floor((double)top_p * 281474976710656.0);
+  return proxy_mask(p, q, k_pool, budget, fx < 1 ? 1 : fx, ordered_blocks, ordered_pages, counts,
+                    hrm_counts, debug_w, debug_hrm, capacity, workspace, workspace_bytes, stream);
 }
 
 COSA_EXPORT cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, const void* k_pool,
@@ -240,7 +267,40 @@ COSA_EXPORT cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, c
   a.skip_record = skip_record;
   a.row_stats = row_stats;
   a.capacity = capacity;
-  a.tau_log2 = skip_tau < 0.f ? -1.f : skip_tau * 1.4426950408889634f;
+  if (skip_tau >= 0.f) {
+    a.skip_mode = cosa::kSkipTau;
+    a.tau_log2 = skip_tau * 1.4426950408889634f;
+  }
+  return hip_status(cosa::launch_attention(a, p->head_dim, p->q_block, true, (hipStream_t)stream));
+}
+
+COSA_EXPORT cosa_status cosa_osk_prefill_delta(const cosa_problem* p, const void* q,
+                                               const void* k_pool, const void* v_pool,
+                                               const int32_t* ordered_blocks,
+                                               const int32_t* ordered_pages, const int32_t* counts,
+                                               int64_t capacity, float skip_delta, void* out,
+                                               float* lse, uint8_t* skip_record,
+                                               int32_t* row_stats, void* stream) {
+  cosa_status st = validate(p);
+  if (st != COSA_OK) return st;
+  if (q == nullptr || k_pool == nullptr || v_pool == nullptr || out == nullptr ||
+      ordered_blocks == nullptr || ordered_pages == nullptr || counts == nullptr)
+    return fail(COSA_ERR_INVALID_ARG, "q, k_pool, v_pool, out and the mask arrays are required");
+  if (capacity < 1) return fail(COSA_ERR_INVALID_ARG, "capacity must be >= 1");
+  if (isnan(skip_delta) || isinf(skip_delta))
+    return fail(COSA_ERR_INVALID_ARG, "skip_delta must be finite");
+  cosa::AttnParams a;
+  fill_attn(a, p, q, k_pool, v_pool, out, lse);
+  a.ordered_blocks = ordered_blocks;
+  a.ordered_pages = ordered_pages;
+  a.counts = counts;
+  a.skip_record = skip_record;
+  a.row_stats = row_stats;
+  a.capacity = capacity;
+  if (skip_delta > 0.f) {
+    a.skip_mode = cosa::kSkipDelta;
+    a.log2_delta = (float)log2((double)skip_delta);
+  }
   return hip_status(cosa::launch_attention(a, p->head_dim, p->q_block, true, (hipStream_t)stream));
 }
 

@@ -38,7 +38,16 @@ struct AttnParams {
   int32_t xcd_groups;             // B*Hkv when it is a multiple of 8, else 0
   int32_t order;                  // tile order, one of TileOrder
   float scale_log2;               // softmax_scale * log2(e)
-  float tau_log2;                 // skip threshold * log2(e); < 0 disables
+  int32_t skip_mode;              // OSK: kSkipOff, kSkipTau or kSkipDelta
+  float tau_log2;                 // kSkipTau: threshold * log2(e)
+  float log2_delta;               // kSkipDelta: log2(Delta); tau = log2(L_b) - log2(Delta)
+};
+
+// In-kernel skip modes of the ordered-skipping kernel.
+enum SkipMode : int32_t {
+  kSkipOff = 0,    // every visited block is computed
+  kSkipTau = 1,    // one threshold for every sequence
+  kSkipDelta = 2   // length-adaptive: threshold ln(L_b / Delta) per sequence
 };
 
 // Arguments of the two KAP kernels.
@@ -58,6 +67,9 @@ struct KapParams {
   int32_t batch, hq, hkv, max_pages, nqb, n_max;
   int32_t beta_ppm;
   float scale;
+  // Top-p mass in fixed point (p * 2^48, rounded down); 0 = budget only,
+  // all ones = p of 1 (keep every candidate the budget allows)
+  uint64_t top_p_fx;
 };
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, bool ordered,

@@ -125,7 +125,14 @@ __device__ __forceinline__ RowStat merge(RowStat x, RowStat y) {
   return o;
 }
 
-template <int D, int R>
+// Top-p mass of a key in fixed point: the key's w rounded down to a multiple
+// of 2^-48 (w * 2^48 is exact in fp32, the conversion truncates).
+__device__ __forceinline__ unsigned long long key_mass(uint32_t key_hi) {
+  const float w = __uint_as_float(0x7FFFFFFFu - (key_hi & 0x7FFFFFFFu));
+  return (unsigned long long)(w * 281474976710656.0f);
+}
+
+template <int D, int R, bool kTopP>
 __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   constexpr int NT = 256;
   constexpr int NWAVE = NT / 64;
@@ -145,7 +152,9 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   __shared__ int sRowA[32];
   __shared__ int sHrm[TPW];          // HRM keys per tile
   __shared__ int sSel[TPW];          // keys kept by the selection
+  __shared__ int sTopK[TPW];         // Top-p: kept count per tile
   __shared__ uint32_t sHist[NWAVE][256];
+  __shared__ unsigned long long sMass[kTopP ? NWAVE : 1][256];   // Top-p only
   uint16_t* sQhi = reinterpret_cast<uint16_t*>(&sKey[0][0]);
   uint16_t* sQlo = sQhi + 32 * D;
 
@@ -433,12 +442,94 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   {
     const int t = wave;
     const int n = n_t[t];
-    const int k = k_t[t];
+    int k = k_t[t];
     int sel = n;                              // keys kept for the final sort
-    if (n > 0 && k < n) {
+    uint32_t top_prefix = 0;
+    bool top_bound = false;                   // the Top-p count decides k
+    if (kTopP && n > 0 && k > 1) {
+      // Top-p: the smallest k whose leading keys (ascending key order = the
+      // visiting order) carry at least the fixed-point mass P.  Radix descent
+      // over the upper 32 key bits with per-digit counts and exact integer
+      // masses; the last digit leaves a group of keys with equal w (same
+      // upper bits) ordered by block index, of which just enough are taken.
+      unsigned long long need = p.top_p_fx;
       uint32_t prefix = 0, pmask = 0;
+      int before_cnt = 0;
+      bool reached = true;
+      for (int shift = 24; shift >= 0 && reached; shift -= 8) {
+        for (int bin = lane; bin < 256; bin += 64) {
+          sHist[t][bin] = 0;
+          sMass[t][bin] = 0ull;
+        }
+        for (int idx = lane; idx < n; idx += 64) {
+          const uint32_t hi = (uint32_t)(sKey[t][idx] >> 32);
+          if ((hi & pmask) == prefix) {
+            const uint32_t d = (hi >> shift) & 255u;
+            atomicAdd(&sHist[t][d], 1u);
+            atomicAdd(&sMass[t][d], key_mass(hi));
+          }
+        }
+        uint32_t c[4];
+        unsigned long long m[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          c[e] = sHist[t][4 * lane + e];
+          m[e] = sMass[t][4 * lane + e];
+        }
+        const uint32_t cmine = c[0] + c[1] + c[2] + c[3];
+        const unsigned long long mmine = m[0] + m[1] + m[2] + m[3];
+        uint32_t cincl = cmine;
+        unsigned long long mincl = mmine;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t oc = __shfl_up(cincl, off);
+          const unsigned long long om = __shfl_up(mincl, off);
+          if (lane >= off) {
+            cincl += oc;
+            mincl += om;
+          }
+        }
+        uint32_t cbefore = cincl - cmine;
+        unsigned long long mbefore = mincl - mmine;
+        int digit = -1, cnt_left = 0;
+        unsigned long long need_left = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (digit < 0 && mbefore < need && mbefore + m[e] >= need) {
+            digit = 4 * lane + e;
+            cnt_left = (int)cbefore;
+            need_left = need - mbefore;
+          }
+          cbefore += c[e];
+          mbefore += m[e];
+        }
+        const unsigned long long found = __ballot(digit >= 0);
+        if (found == 0ull) {
+          reached = false;   // the whole tile holds less than P: every key
+        } else {
+          const int src = __ffsll((long long)found) - 1;
+          digit = __shfl(digit, src);
+          before_cnt += __shfl(cnt_left, src);
+          need = __shfl(need_left, src);
+          prefix |= (uint32_t)digit << shift;
+          pmask |= 0xFFu << shift;
+        }
+      }
+      if (reached) {
+        const unsigned long long wq = key_mass(prefix);   // > 0: its group holds need > 0
+        const int kp = before_cnt + (int)((need + wq - 1) / wq);
+        if (kp < k) {
+          k = kp;
+          top_bound = true;
+          top_prefix = prefix;
+        }
+      }
+      if (lane == 0) sTopK[t] = k;
+    }
+    if (n > 0 && k < n) {
+      uint32_t prefix = top_prefix, pmask = top_bound ? 0xFFFFFFFFu : 0u;
       int need = k;
-      for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int shift = 24; shift >= 0 && !top_bound; shift -= 8) {
         for (int bin = lane; bin < 256; bin += 64) sHist[t][bin] = 0;
         for (int idx = lane; idx < n; idx += 64) {
           const uint32_t hi = (uint32_t)(sKey[t][idx] >> 32);
@@ -487,6 +578,11 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     if (lane == 0) sSel[t] = sel;
   }
   __syncthreads();
+  if (kTopP) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      if (n_t[t] > 0 && k_t[t] > 1) k_t[t] = sTopK[t];
+  }
   int npow_sel = 1;
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
@@ -548,6 +644,7 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
 
 template <int D, int R>
 hipError_t launch_kap_t(const KapParams& p, hipStream_t stream) {
+  const bool top_p = p.top_p_fx != 0;
   const int nkb = p.n_max;
   if (p.batch <= 0 || nkb <= 0) return hipSuccess;
   hipLaunchKernelGGL((kap_pool_keys<D>), dim3(nkb, p.batch), dim3(256), 0, stream, p);
@@ -555,7 +652,10 @@ hipError_t launch_kap_t(const KapParams& p, hipStream_t stream) {
   if (err != hipSuccess) return err;
   const int64_t groups = (p.nqb + kTilesPerGroup - 1) / kTilesPerGroup;
   const int64_t grid = (int64_t)p.batch * p.hq * groups;
-  hipLaunchKernelGGL((kap_select<D, R>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  if (top_p)
+    hipLaunchKernelGGL((kap_select<D, R, true>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((kap_select<D, R, false>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

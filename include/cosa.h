@@ -151,6 +151,29 @@ cosa_status cosa_proxy_ordered_mask(const cosa_problem* p, const void* q, const 
                                     void* stream);
 
 /*
+ * Kernel-Aware Proxy with stage-1 Top-p (CoSA (paperpeel) §5.1
+ * "Hyperparameters" and App. D.1: Top-p selection, p = 0.95 for Qwen3-8B).
+ *
+ * As cosa_proxy_ordered_mask(), except that the kept count of a tile is
+ *   k = min(budget count, Top-p count),
+ * the Top-p count being the smallest k >= 1 such that the first k blocks of
+ * the HRM-first order carry at least the mass p, where the mass of a block
+ * is its importance w_j (the w_j of a tile sum to 1).  The sum is taken
+ * exactly in fixed point: every w_j (the fp32 value debug_w reports) is
+ * rounded down to a multiple of 2^-48 and p to floor(p * 2^48) * 2^-48, so
+ * the count depends on neither summation order nor run.  top_p = 1 keeps
+ * every candidate the budget allows; if the masses never reach p, likewise.
+ * top_p must lie in (0, 1]; budget (the cap, 1 for none) and capacity as for
+ * cosa_proxy_ordered_mask().
+ */
+cosa_status cosa_proxy_ordered_mask_top_p(const cosa_problem* p, const void* q,
+                                          const void* k_pool, float top_p, float budget,
+                                          int32_t* ordered_blocks, int32_t* ordered_pages,
+                                          int32_t* counts, int32_t* hrm_counts, float* debug_w,
+                                          uint8_t* debug_hrm, int64_t capacity, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/*
  * Ordered-Skipping Kernel (CoSA (paperpeel) §4.3, App. D.1; skip rule §3.3).
  *
  * For every mask row (b, h, i) the kernel walks slots t = 0..counts[row]-1 in
@@ -179,6 +202,24 @@ cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, const void* k
                              const int32_t* ordered_pages, const int32_t* counts,
                              int64_t capacity, float skip_tau, void* out, float* lse,
                              uint8_t* skip_record, int32_t* row_stats, void* stream);
+
+/*
+ * Ordered-Skipping Kernel with the length-adaptive threshold Delta / N
+ * (CoSA (paperpeel) §5.1 "Hyperparameters", App. D.1: Delta = 2000 for
+ * Qwen3-8B, 200 for Llama-3.1-8B, Delta = -1 disables the skip).
+ *
+ * As cosa_osk_prefill(), with the threshold of sequence b of L_b tokens
+ * tau_b = ln(L_b / skip_delta) nats (Delta / N read as the bound on
+ * exp(block max - running max)).  skip_delta > 0 turns the skip on whatever
+ * the sign of tau_b (a sequence shorter than Delta then keeps only blocks
+ * that raise some row's max); skip_delta <= 0 turns it off.  skip_delta must
+ * be finite.
+ */
+cosa_status cosa_osk_prefill_delta(const cosa_problem* p, const void* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* ordered_blocks,
+                                   const int32_t* ordered_pages, const int32_t* counts,
+                                   int64_t capacity, float skip_delta, void* out, float* lse,
+                                   uint8_t* skip_record, int32_t* row_stats, void* stream);
 
 /*
  * Dense causal prefill on the same kernel: every tile visits all of its

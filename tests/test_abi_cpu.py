@@ -129,6 +129,20 @@ def test_entry_points_reject_bad_buffers(lib):
                                        None) == _lib.COSA_ERR_WORKSPACE
     assert lib.cosa_proxy_ordered_mask(pr, 1, 1, 0.0, 1, 1, 1, None, None, None, cap, 1, ws,
                                        None) == E
+    # Top-p outside (0, 1], a bad cap and a short capacity are refused before any launch
+    for bad_p in (0.0, -0.5, 1.01, float("nan")):
+        assert lib.cosa_proxy_ordered_mask_top_p(pr, 1, 1, bad_p, 0.1, 1, 1, 1, None, None, None,
+                                                 cap, 1, ws, None) == E
+    assert lib.cosa_proxy_ordered_mask_top_p(pr, 1, 1, 0.9, 0.0, 1, 1, 1, None, None, None, cap,
+                                             1, ws, None) == E
+    assert lib.cosa_proxy_ordered_mask_top_p(pr, 1, 1, 0.9, 0.1, 1, 1, 1, None, None, None,
+                                             cap - 1, 1, ws, None) == E
+    # Delta must be finite; the mask arrays are required
+    for bad_d in (float("nan"), float("inf"), float("-inf")):
+        assert lib.cosa_osk_prefill_delta(pr, 1, 1, 1, 1, 1, 1, 5, bad_d, 1, None, None, None,
+                                          None) == E
+    assert lib.cosa_osk_prefill_delta(pr, 1, 1, 1, None, 1, 1, 5, 200.0, 1, None, None, None,
+                                      None) == E
     # the proxy handles at most 2048 key blocks per sequence
     big = _problem(max_seqlen=131073, max_pages_per_seq=2049, total_q=131073)
     assert lib.cosa_proxy_ordered_mask(ctypes.byref(big), 1, 1, 0.1, 1, 1, 1, None, None, None,

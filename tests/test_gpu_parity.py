@@ -6,6 +6,8 @@ Tolerances: max-abs 2e-2 / mean-abs 2e-3 on outputs for the same visited set;
 masks and page remaps bit-exact except near-ties of the oracle's own scores;
 skip sets identical except slots within 1e-3 nats of the threshold (counted).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -77,7 +79,9 @@ def test_dense_matches_oracle(case):
     ls.assert_ok(max_abs=1e-3, mean_abs=1e-4, label=f"dense {name} lse")
 
 
-def _run_osk_vs_oracle(w, x, blocks, counts, tau, label, tiles=None):
+def _run_osk_vs_oracle(w, x, blocks, counts, tau, label, tiles=None, delta=None):
+    """OSK through the C ABI against the closed-form oracle tile by tile; with
+    ``delta`` the length-adaptive entry point and tau_b = ln(L_b / delta)."""
     prob, q, k, v = upload(x, DEV)
     C = blocks.shape[-1]
     pages = np.where(blocks >= 0, 0, -1).astype(np.int32)
@@ -87,7 +91,10 @@ def _run_osk_vs_oracle(w, x, blocks, counts, tau, label, tiles=None):
     mask = bk.OrderedMask(blocks=torch.from_numpy(blocks).to(DEV),
                           pages=torch.from_numpy(pages).to(DEV),
                           counts=torch.from_numpy(counts).to(DEV), hrm_counts=None, capacity=C)
-    res = bk.osk_prefill(prob, q, k, v, mask, tau)
+    if delta is None:
+        res = bk.osk_prefill(prob, q, k, v, mask, tau)
+    else:
+        res = bk.osk_prefill_delta(prob, q, k, v, mask, delta)
     torch.cuda.synchronize()
     out, lse, rec, stats = _np(res.out), _np(res.lse), _np(res.skip_record), _np(res.row_stats)
     st, ls = ErrStats(), ErrStats()
@@ -101,6 +108,11 @@ def _run_osk_vs_oracle(w, x, blocks, counts, tau, label, tiles=None):
         kk = materialise(x.k_pool, x.page_table[b], L, w.page_size)
         vv = materialise(x.v_pool, x.page_table[b], L, w.page_size)
         nqb = (L + w.q_block - 1) // w.q_block
+        if delta is None:
+            tau_b, on = tau, tau >= 0
+        else:
+            on = delta > 0
+            tau_b = oosk.tau_from_delta(L, delta) if on else -1.0
         for h in range(w.num_q_heads):
             g = h // grp
             for i in range(nqb):
@@ -110,8 +122,8 @@ def _run_osk_vs_oracle(w, x, blocks, counts, tau, label, tiles=None):
                 cnt = int(counts[b, h, i])
                 bl = blocks[b, h, i, :cnt]
                 qr = x.q[s0 + rows, h].astype(np.float64)
-                r = oosk.osk_tile_closed_form(qr, rows, kk[:, g], vv[:, g], bl, tau,
-                                              w.softmax_scale, w.page_size)
+                r = oosk.osk_tile_closed_form(qr, rows, kk[:, g], vv[:, g], bl, tau_b,
+                                              w.softmax_scale, w.page_size, skip_on=on)
                 near_total += check_osk_tile(out[s0 + rows, h], lse[h, s0 + rows],
                                              rec[b, h, i], r, qr, rows, kk[:, g], vv[:, g], bl,
                                              w.softmax_scale, w.page_size, st, ls)
@@ -226,3 +238,104 @@ def test_deterministic_and_poison_safe():
     assert np.isnan(x.k_pool).any()
     for t in (outs[0][3], outs[0][6]):
         assert torch.isfinite(t.float()).all()
+
+
+# ---------------------------------------------------------------------------
+# Length-adaptive threshold Delta / N (cosa_osk_prefill_delta)
+
+SKIP_RAGGED = dict(seqlens=(700, 1500, 90), shuffled_pages=True, spare_pages=5,
+                   precision="bf16")
+
+
+@pytest.mark.parametrize("delta", [-1.0, 50.0, 200.0, 2000.0])
+def test_osk_delta_per_sequence_threshold(delta):
+    # tau_b = ln(L_b / delta): 2.64 / 3.40 / 0.59 nats at delta 50 and negative
+    # (skip still on) for the shorter sequences at delta 2000
+    w, x = _inputs("tiny_skip", **SKIP_RAGGED)
+    print(f"[case] osk delta={delta} seqlens={w.seqlens}", flush=True)
+    m = okap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
+                                w.q_block, w.page_size, w.budget, w.softmax_scale)
+    n = _run_osk_vs_oracle(w, x, m.blocks, m.counts, 0.0, f"osk delta={delta}", delta=delta)
+    if delta > 0:
+        assert n > 0
+    else:
+        assert n == 0
+
+
+# ---------------------------------------------------------------------------
+# Stage-1 Top-p (cosa_proxy_ordered_mask_top_p)
+
+TOP_P_TOL = 1e-5   # fp32 importance scores against fp64: mass near-ties
+
+
+def _fixed_point_selection(w32, hrm, n, beta_ppm, top_p):
+    """The documented selection applied to the GPU's own fp32 w and HRM flags:
+    HRM-first order, budget count, Top-p count over w rounded down to 2^-48."""
+    w32 = np.asarray(w32[:n], dtype=np.float32)
+    order = okap.flag_grouped_order(w32.astype(np.float64), np.asarray(hrm[:n], dtype=bool))
+    k = okap.budget_count(n, beta_ppm)
+    if top_p < 1.0:
+        fx = np.floor(w32.astype(np.float64) * 2.0 ** 48).astype(np.int64)
+        target = int(np.floor(np.float64(np.float32(top_p)) * 2.0 ** 48))
+        cum = np.cumsum(fx[order])
+        hit = np.flatnonzero(cum >= target)
+        k = min(k, int(hit[0]) + 1 if hit.size else n)
+    return order[:k]
+
+
+def _allowed_counts(tile, top_p, beta_ppm):
+    kb = okap.budget_count(tile.n, beta_ppm)
+    if top_p >= 1.0:
+        return {kb}
+    cum = np.concatenate([[0.0], np.cumsum(tile.w[tile.order])])
+    ok = {tile.k}
+    for kp in range(1, tile.n + 1):
+        if cum[kp - 1] < top_p + TOP_P_TOL and cum[kp] >= top_p - TOP_P_TOL:
+            ok.add(min(kb, kp))
+    return ok
+
+
+@pytest.mark.parametrize("case", [("tiny", {}, 0.5, 1.0), ("tiny", {}, 0.95, 1.0),
+                                  ("tiny_skip", {}, 0.8, 1.0), ("tiny", dict(RAGGED), 0.9, 0.3),
+                                  ("tiny", dict(RAGGED, q_block=64), 0.95, 1.0),
+                                  ("tiny", dict(RAGGED), 1.0, 0.5)])
+def test_kap_top_p_matches_oracle(case):
+    name, kw, top_p, cap = case
+    w, x = _inputs(name, **kw)
+    print(f"[case] kap top_p={top_p} cap={cap} {name} {kw}", flush=True)
+    prob, q, k, v = upload(x, DEV)
+    gm = bk.proxy_ordered_mask_top_p(prob, q, k, top_p, cap, debug=True)
+    torch.cuda.synchronize()
+    gb, gp, gc, gh = _np(gm.blocks), _np(gm.pages), _np(gm.counts), _np(gm.hrm_counts)
+    dw, dh = _np(gm.debug_w), _np(gm.debug_hrm)
+    beta = okap.budget_ppm(cap)
+    exact = ties = shorter = 0
+    grp = w.num_q_heads // w.num_kv_heads
+    for b in range(w.batch):
+        s0, L = int(x.cu_seqlens[b]), int(x.seqlens[b])
+        nqb = (L + w.q_block - 1) // w.q_block
+        assert np.all(gc[b, :, nqb:] == 0)
+        if L == 0:
+            continue
+        kk = materialise(x.k_pool, x.page_table[b], L, w.page_size)
+        for h in range(w.num_q_heads):
+            res = okap.head_tiles(x.q[s0:s0 + L, h].astype(np.float64), kk[:, h // grp],
+                                  w.softmax_scale, w.q_block, w.page_size, beta, top_p=top_p)
+            for i, tile in res.items():
+                c = int(gc[b, h, i])
+                # 1) bit-exact: the documented rule on the kernel's own w and flags
+                want = _fixed_point_selection(dw[b, h, i], dh[b, h, i], tile.n, beta, top_p)
+                assert c == len(want) and np.array_equal(gb[b, h, i, :c], want), (b, h, i)
+                # 2) against the fp64 oracle: the count up to mass near-ties,
+                #    then the kept blocks as for the budget mask
+                assert c in _allowed_counts(tile, top_p, beta), (b, h, i, c, tile.k)
+                shorter += c < tile.n
+                kind = check_kap_row(gb[b, h, i], gp[b, h, i], c, gh[b, h, i],
+                                     dataclasses.replace(tile, k=c), x.page_table[b])
+                exact += kind == "exact" and c == tile.k
+                ties += kind == "tie" or c != tile.k
+    print(f"[parity] kap top_p={top_p} cap={cap}: rows exact={exact} near-tie={ties} "
+          f"truncated={shorter}")
+    assert exact > 0 and ties <= max(1, exact // 100)
+    if top_p < 1.0:
+        assert shorter > 0
