@@ -23,6 +23,8 @@ Modules
 ``osk``     Ordered-Skipping Kernel: sequential online-softmax loop over the
             ordered mask with the tile-wide in-kernel skip, and an independent
             closed form of the same result.
+``fidelity`` the KAP kept set against the top-k blocks by exact attention
+            mass at a matched budget (IoU, mass recall).
 
 Pinning.  Each function is pinned by ``tests/test_oracle_*.py`` (``-m "not gpu"``)
 to closed forms, library routines (``torch`` SDPA in float64 on the CPU),
@@ -35,4 +37,4 @@ the paper's own numbers (none are printed).
 All floating point here is float64.  Inputs are the bf16-rounded values the
 GPU sees, widened exactly to float64.
 """
-from . import dense, kap, osk, paging  # noqa: F401
+from . import dense, fidelity, kap, osk, paging  # noqa: F401

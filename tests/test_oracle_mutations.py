@@ -12,9 +12,11 @@ import textwrap
 import pytest
 
 import oracle.dense as dense
+import oracle.fidelity as fid
 import oracle.kap as kap
 import oracle.osk as osk
 import tests.test_oracle_dense as td
+import tests.test_oracle_fidelity as tf
 import tests.test_oracle_kap as tk
 import tests.test_oracle_osk as to
 
@@ -91,6 +93,12 @@ MUTATIONS = [
     # Delta / N: threshold inverted to ln(Delta / N)
     (osk, "tau_from_delta", "math.log(seqlen / delta)", "math.log(delta / seqlen)",
      [to.test_tau_from_delta_hand_values]),
+    # fidelity: exact top-k picks the smallest masses
+    (fid, "top_mass_blocks", "-mass))", "mass))",
+     [tf.test_top_mass_and_iou_hand_values]),
+    # fidelity: the diagonal key dropped from the exact mass
+    (fid, "exact_block_mass", "<= row_pos[:, None]", "< row_pos[:, None]",
+     [tf.test_uniform_attention_block_mass_by_hand]),
     # Delta / N: skip switched off whenever tau_b comes out negative
     (osk, "osk_prefill", "on = delta > 0", "on = delta > 0 and tau_from_delta(L, delta) >= 0",
      [lambda: to.test_delta_mode_negative_tau_still_skips(False)]),
