@@ -51,6 +51,12 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="also time the workload's budget x tau sweep and the Top-p / Delta "
                          "operating points (extra JSON lines)")
+    ap.add_argument("--remap-ablation", action="store_true",
+                    help="also time the OSK on the same kept sets in KAP order and in ascending "
+                         "block order over the workload's budget x tau sweep (extra JSON lines)")
+    ap.add_argument("--logical-skip", action="store_true",
+                    help="also time physical page jumping (OSK, skip off) against logical mask "
+                         "skipping (cosa_block_mask_prefill) on the same kept sets (extra lines)")
     ap.add_argument("--only", choices=["all", "kap", "osk", "dense"], default="all",
                     help="launch only one kernel kind (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -242,6 +248,15 @@ def main():
                                   "stage1_budget": round(vis / causal_slots, 5),
                                   "skip_ratio": round(skp / max(vis, 1), 5),
                                   "osk_tflops": round(fl / om / 1e9, 1)}), flush=True)
+    if args.logical_skip:
+        logical_skip_bench(args, w, bk, prob, q, kp, vp, ws, out, stream, ev, causal_slots,
+                           dense_ms)
+
+    if args.remap_ablation:
+        remap_ablation(args, w, bk, prob, q, kp, vp, ws, out, stream, ev, causal_slots, fps,
+                       dense_ms)
+
+    if args.sweep:
         # the pages' own knobs: stage-1 Top-p (no budget cap) with the
         # length-adaptive threshold ln(N / Delta)
         for p_, d_ in TOP_P_DELTA_POINTS:
@@ -271,6 +286,89 @@ def main():
                               "skip_ratio": round(skp / max(vis, 1), 5),
                               "effective_budget": round((vis - skp) / causal_slots, 5),
                               "osk_tflops": round(fl / om / 1e9, 1)}), flush=True)
+
+
+def ascending_copy(bk, torch, prob, mask):
+    """The same kept sets with every row sorted by block index (no remapping
+    of the visiting order), pages looked up again from the page table."""
+    big = torch.iinfo(torch.int32).max
+    blocks = torch.where(mask.blocks < 0, torch.full_like(mask.blocks, big), mask.blocks)
+    blocks = torch.sort(blocks, dim=-1).values
+    blocks = torch.where(blocks == big, torch.full_like(blocks, -1), blocks)
+    B = prob.batch
+    flat = blocks.reshape(B, -1).long()
+    pages = torch.gather(prob.page_table.long(), 1, flat.clamp(min=0))
+    pages = torch.where(flat < 0, torch.full_like(pages, -1), pages)
+    return bk.OrderedMask(blocks=blocks.contiguous(), pages=pages.to(torch.int32).reshape(
+        blocks.shape).contiguous(), counts=mask.counts, hrm_counts=None, capacity=mask.capacity)
+
+
+def remap_ablation(args, w, bk, prob, q, kp, vp, ws, out, stream, ev, causal_slots, fps,
+                   dense_ms):
+    """Skip ratio and OSK time with the KAP order against ascending order on
+    the same visited sets (the kernel-side analogue of the remapping ablation:
+    the in-kernel skip fires more often when the HRM blocks come first)."""
+    import torch
+    for b_ in (w.budgets_sweep or (w.budget,)):
+        m_kap = bk.proxy_ordered_mask(prob, q, kp, b_, workspace=ws)
+        m_asc = ascending_copy(bk, torch, prob, m_kap)
+        for t_ in (w.taus_sweep or (w.tau,)):
+            for order, m2 in (("kap", m_kap), ("ascending", m_asc)):
+                r2 = bk.osk_prefill(prob, q, kp, vp, m2, t_, record=True)
+                torch.cuda.synchronize()
+                st = r2.row_stats.cpu().numpy().reshape(-1, 2)
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                for _ in range(args.steps):
+                    bk.osk_prefill(prob, q, kp, vp, m2, t_, out=out)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                om = e0.elapsed_time(e1) / args.steps
+                vis, skp = int(st[:, 0].sum()), int(st[:, 1].sum())
+                print(json.dumps({"remap_ablation": w.name, "budget": b_, "tau": t_,
+                                  "order": order, "osk_ms": round(om, 4),
+                                  "stage1_budget": round(vis / causal_slots, 5),
+                                  "skip_ratio": round(skp / max(vis, 1), 5),
+                                  "effective_budget": round((vis - skp) / causal_slots, 5),
+                                  "speedup_vs_dense": None if dense_ms is None else
+                                  round(dense_ms / om, 3),
+                                  "osk_tflops": round(fps * (2 * vis - skp) / om / 1e9, 1)}),
+                      flush=True)
+
+
+LOGICAL_SKIP_BUDGETS = (0.5, 0.3, 0.2, 0.1, 0.05)
+
+
+def logical_skip_bench(args, w, bk, prob, q, kp, vp, ws, out, stream, ev, causal_slots,
+                       dense_ms):
+    """Physical page jumping (the OSK over the kept list, no in-kernel skip)
+    against logical mask skipping (every causal block walked, unselected ones
+    dropped inside the loop) on the same kept sets, per budget."""
+    import torch
+    from block_sparse_long_kap_amd.masks import block_bitmask
+    for b_ in LOGICAL_SKIP_BUDGETS:
+        m2 = bk.proxy_ordered_mask(prob, q, kp, b_, workspace=ws)
+        bits = block_bitmask(prob, m2)
+        vis = int(m2.counts.sum().item())
+        for _ in range(max(1, args.warmup)):
+            bk.osk_prefill(prob, q, kp, vp, m2, -1.0, out=out)
+            bk.block_mask_prefill(prob, q, kp, vp, bits, out=out)
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        for _ in range(args.steps):
+            bk.osk_prefill(prob, q, kp, vp, m2, -1.0, out=out)
+        e1.record(stream)
+        for _ in range(args.steps):
+            bk.block_mask_prefill(prob, q, kp, vp, bits, out=out)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        jm, lm = e0.elapsed_time(e1) / args.steps, e1.elapsed_time(e2) / args.steps
+        print(json.dumps({"logical_skip": w.name, "budget": b_,
+                          "stage1_budget": round(vis / causal_slots, 5),
+                          "jump_ms": round(jm, 4), "logical_ms": round(lm, 4),
+                          "jump_speedup_over_logical": round(lm / jm, 3),
+                          "dense_ms": None if dense_ms is None else round(dense_ms, 4)}),
+              flush=True)
 
 
 def cpu_baseline(w, x, budget, tau, n_tiles):

@@ -274,6 +274,30 @@ def dense_prefill(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor, v_poo
     return out
 
 
+def block_mask_prefill(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor,
+                       v_pool: torch.Tensor, block_mask: torch.Tensor, *, lse: bool = True,
+                       out: Optional[PrefillOutput] = None) -> PrefillOutput:
+    """Logical mask skipping over every causal block (``cosa_block_mask_prefill``);
+    block_mask is int32 [B][Hq][NQB][words] holding uint32 bit patterns."""
+    lib = _lib.load()
+    problem._check_qkv(q, k_pool, v_pool)
+    dev = problem.device
+    rows = (problem.batch, problem.num_q_heads, problem.num_q_tiles())
+    _need(block_mask, "block_mask", torch.int32, dev, ndim=4)
+    if tuple(block_mask.shape[:3]) != rows:
+        raise ValueError(f"block_mask rows {tuple(block_mask.shape[:3])} != {rows}")
+    if out is None:
+        out = PrefillOutput(
+            out=torch.empty_like(q),
+            lse=torch.empty((problem.num_q_heads, problem.total_q), dtype=torch.float32,
+                            device=dev) if lse else None)
+    st = lib.cosa_block_mask_prefill(problem.ref(), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                     _ptr(block_mask), block_mask.shape[-1], _ptr(out.out),
+                                     _ptr(out.lse), _stream(dev))
+    _lib.check(st, "cosa_block_mask_prefill")
+    return out
+
+
 def tau_from_delta(seqlen: int, delta: float) -> float:
     """Skip threshold in nats from the length-adaptive scale Delta.
 

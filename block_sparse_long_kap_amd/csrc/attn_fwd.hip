@@ -8,7 +8,10 @@
 // (App. D.1: one tile-wide vote combined from the row-wise predicates, made
 // from the on-chip online-softmax maxima with no extra logits and no extra
 // global-memory traffic).  Dense mode walks every causal block in ascending
-// order through the page table and never votes.
+// order through the page table and never votes.  Logical mode walks the same
+// blocks but computes only those selected by a block bitmask, paying the loop
+// and the per-block barrier on the others (the logical mask skipping that
+// App. D.3 / Fig. B compares physical page jumping against).
 //
 // gfx950 mapping (one workgroup = one query tile of one query head):
 //   * NW wavefronts of 64 lanes, 32 query rows per wavefront (tile = 32*NW).
@@ -121,8 +124,10 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, int bid, int& b
   }
 }
 
-template <int D, int NW, bool kOrdered>
+template <int D, int NW, int kMode>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p) {
+  constexpr bool kOrdered = kMode == kModeOrdered;
+  constexpr bool kLogical = kMode == kModeLogical;
   constexpr int NT = NW * 64;
   constexpr int BQ = NW * 32;
   constexpr int KCH = D / 8;                         // 16-byte chunks per key row
@@ -147,6 +152,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   __shared__ __attribute__((aligned(16))) unsigned char sV1[D * VLayout::kStride];
   __shared__ int sVote[2][NW];
   __shared__ int sSlot[2][2][64];   // [page | block][ring chunk][slot]
+  // logical-skip mode: the tile's block bitmask (up to 16384 causal blocks)
+  __shared__ uint32_t sBits[kLogical ? 512 : 1];
   auto kbuf = [&](int buf) -> unsigned char* { return buf ? sK1 : sK0; };
   auto vbuf_of = [&](int buf) -> unsigned char* { return buf ? sV1 : sV0; };
 
@@ -173,6 +180,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   }
   const int tile_last = min(tile_q0 + BQ, L) - 1;
   const int cnt = kOrdered ? p.counts[row] : tile_last / kPage + 1;
+  if (kLogical) {
+    const uint32_t* bits = p.block_mask + row * p.mask_words;
+    for (int wd = tid; wd < (cnt + 31) / 32; wd += NT) sBits[wd] = bits[wd];
+  }
+  // logical-skip mode: is causal block t selected (uniform)
+  auto selected = [&](int t) -> bool {
+    if constexpr (kLogical)
+      return (__builtin_amdgcn_readfirstlane(sBits[t >> 5]) >> (t & 31)) & 1u;
+    else
+      return true;
+  };
   // read-only for the whole kernel: lets the uniform slot lookups go
   // through scalar loads instead of vector loads plus a vmcnt wait
   const int32_t* __restrict__ ob = kOrdered ? p.ordered_blocks + row * p.capacity : nullptr;
@@ -213,7 +231,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       if (kOrdered) sSlot[1][c][lane] = chunk_entry(ob, c);
     }
   }
-  __syncthreads();   // every wave reads the ring that wave 0 just filled
+  __syncthreads();   // every wave reads the ring (and bitmask) just filled
   int pend_pg = 0, pend_bl = 0, pend_chunk = -1;
   auto slot_page = [&](int t) -> int {
     return __builtin_amdgcn_readfirstlane(sSlot[0][(t >> 6) & 1][t & 63]);
@@ -408,12 +426,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   int j_cur = 0, j_next = 0;
   if (cnt > 0) {
     j_cur = slot_block(0);
-    copy_k(slot_page(0), 0);
+    if (selected(0)) copy_k(slot_page(0), 0);
     if (cnt > 1) {
       j_next = slot_block(1);
-      copy_k(slot_page(1), 1);
+      if (selected(1)) copy_k(slot_page(1), 1);
     }
-    load_v(slot_page(0));
+    if (selected(0)) load_v(slot_page(0));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -421,8 +439,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     advance_chunks(t + 1);   // chunk holding slot t+1 (and t+2) is current
     const int buf = t & 1;
     const int key0 = j_cur * kPage;
+    const bool sel = selected(t);
     // some key of the page is visible to some valid row of this wave
-    const bool active = wave_has_rows && key0 <= wave_last;
+    const bool active = sel && wave_has_rows && key0 <= wave_last;
     f32x16_t sacc[2];
     float bm = kNegInf;
     if (active) {
@@ -430,7 +449,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       bm = mask_max(j_cur, sacc);
     }
     vote(bm, buf);
-    store_v(buf, j_cur);
+    if (sel) store_v(buf, j_cur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -450,9 +469,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     const int j_after = j_next;
     if (t + 2 < cnt) {
       j_next = slot_block(t + 2);
-      copy_k(slot_page(t + 2), buf);
+      if (selected(t + 2)) copy_k(slot_page(t + 2), buf);
     }
-    if (t + 1 < cnt) load_v(slot_page(t + 1));
+    if (t + 1 < cnt && selected(t + 1)) load_v(slot_page(t + 1));
 
     if (active && !skip) {
       // ---- online softmax (log2 domain) with lazy rescaling
@@ -507,23 +526,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   }
 }
 
-template <int D, int NW, bool kOrdered>
+template <int D, int NW, int kMode>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.batch * p.hq * p.nqb;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, kOrdered>), dim3((unsigned)grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, kMode>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, bool ordered,
+hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, AttnMode mode,
                             hipStream_t stream) {
 #define COSA_ATTN_CASE(D_, BQ_)                                                       \
-  if (head_dim == D_ && q_block == BQ_)                                               \
-    return ordered ? launch_one<D_, BQ_ / 32, true>(p, stream)                        \
-                   : launch_one<D_, BQ_ / 32, false>(p, stream);
+  if (head_dim == D_ && q_block == BQ_) {                                             \
+    if (mode == kModeOrdered) return launch_one<D_, BQ_ / 32, kModeOrdered>(p, stream); \
+    if (mode == kModeLogical) return launch_one<D_, BQ_ / 32, kModeLogical>(p, stream); \
+    return launch_one<D_, BQ_ / 32, kModeDense>(p, stream);                           \
+  }
   COSA_ATTN_CASE(128, 128)
   COSA_ATTN_CASE(128, 64)
   COSA_ATTN_CASE(64, 128)

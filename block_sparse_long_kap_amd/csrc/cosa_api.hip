@@ -93,6 +93,8 @@ void fill_attn(cosa::AttnParams& a, const cosa_problem* p, const void* q, const 
   a.counts = nullptr;
   a.skip_record = nullptr;
   a.row_stats = nullptr;
+  a.block_mask = nullptr;
+  a.mask_words = 0;
   a.capacity = 0;
   a.total_q = p->total_q;
   a.batch = p->batch;
@@ -271,7 +273,8 @@ COSA_EXPORT cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, c
     a.skip_mode = cosa::kSkipTau;
     a.tau_log2 = skip_tau * 1.4426950408889634f;
   }
-  return hip_status(cosa::launch_attention(a, p->head_dim, p->q_block, true, (hipStream_t)stream));
+  return hip_status(
+      cosa::launch_attention(a, p->head_dim, p->q_block, cosa::kModeOrdered, (hipStream_t)stream));
 }
 
 COSA_EXPORT cosa_status cosa_osk_prefill_delta(const cosa_problem* p, const void* q,
@@ -301,7 +304,8 @@ COSA_EXPORT cosa_status cosa_osk_prefill_delta(const cosa_problem* p, const void
     a.skip_mode = cosa::kSkipDelta;
     a.log2_delta = (float)log2((double)skip_delta);
   }
-  return hip_status(cosa::launch_attention(a, p->head_dim, p->q_block, true, (hipStream_t)stream));
+  return hip_status(
+      cosa::launch_attention(a, p->head_dim, p->q_block, cosa::kModeOrdered, (hipStream_t)stream));
 }
 
 COSA_EXPORT cosa_status cosa_dense_prefill(const cosa_problem* p, const void* q,
@@ -313,5 +317,25 @@ COSA_EXPORT cosa_status cosa_dense_prefill(const cosa_problem* p, const void* q,
     return fail(COSA_ERR_INVALID_ARG, "q, k_pool, v_pool and out are required");
   cosa::AttnParams a;
   fill_attn(a, p, q, k_pool, v_pool, out, lse);
-  return hip_status(cosa::launch_attention(a, p->head_dim, p->q_block, false, (hipStream_t)stream));
+  return hip_status(
+      cosa::launch_attention(a, p->head_dim, p->q_block, cosa::kModeDense, (hipStream_t)stream));
+}
+
+COSA_EXPORT cosa_status cosa_block_mask_prefill(const cosa_problem* p, const void* q,
+                                                const void* k_pool, const void* v_pool,
+                                                const uint32_t* block_mask, int64_t mask_words,
+                                                void* out, float* lse, void* stream) {
+  cosa_status st = validate(p);
+  if (st != COSA_OK) return st;
+  if (q == nullptr || k_pool == nullptr || v_pool == nullptr || out == nullptr ||
+      block_mask == nullptr)
+    return fail(COSA_ERR_INVALID_ARG, "q, k_pool, v_pool, block_mask and out are required");
+  if (mask_words < ceil_div(ceil_div(p->max_seqlen, p->kv_block), 32))
+    return fail(COSA_ERR_INVALID_ARG, "mask_words < ceil(ceil(max_seqlen / kv_block) / 32)");
+  cosa::AttnParams a;
+  fill_attn(a, p, q, k_pool, v_pool, out, lse);
+  a.block_mask = block_mask;
+  a.mask_words = mask_words;
+  return hip_status(
+      cosa::launch_attention(a, p->head_dim, p->q_block, cosa::kModeLogical, (hipStream_t)stream));
 }

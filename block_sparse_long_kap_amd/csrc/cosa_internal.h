@@ -32,6 +32,8 @@ struct AttnParams {
   const int32_t* counts;          // OSK only
   uint8_t* skip_record;           // OSK only, nullable
   int32_t* row_stats;             // OSK only, nullable
+  const uint32_t* block_mask;     // logical-skip mode only: [rows][mask_words] bits
+  int64_t mask_words;
   int64_t capacity;
   int64_t total_q;
   int32_t batch, hq, hkv, max_pages, nqb;
@@ -41,6 +43,14 @@ struct AttnParams {
   int32_t skip_mode;              // OSK: kSkipOff, kSkipTau or kSkipDelta
   float tau_log2;                 // kSkipTau: threshold * log2(e)
   float log2_delta;               // kSkipDelta: log2(Delta); tau = log2(L_b) - log2(Delta)
+};
+
+// Page-walk modes of the attention kernel.
+enum AttnMode : int32_t {
+  kModeDense = 0,    // every causal block, ascending
+  kModeOrdered = 1,  // the blocks of the ordered mask, in its order (OSK)
+  kModeLogical = 2   // every causal block, ascending, computing only those whose
+                     // bit is set in a block bitmask (logical mask skipping)
 };
 
 // In-kernel skip modes of the ordered-skipping kernel.
@@ -72,7 +82,7 @@ struct KapParams {
   uint64_t top_p_fx;
 };
 
-hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, bool ordered,
+hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, AttnMode mode,
                             hipStream_t stream);
 hipError_t launch_kap(const KapParams& p, int head_dim, int q_block, hipStream_t stream);
 

@@ -125,6 +125,16 @@ STRESS = Workload(
     outlier_channels=5, outlier_scale=10.0,
 )
 
+# Remapping ablation: no sink, a strong local band (about 12.7 nats above the
+# noise at D 128) and no query push, so the row maxima sit on the last blocks
+# of each tile's causal range.  Visiting the HRM blocks first establishes the
+# running max at once; ascending order reaches it only at the end.
+REMAP_32K = LLAMA_32K.with_(
+    name="remap32k", seed=6, budget=0.3, tau=6.0,
+    pattern=HeadPattern(sink=False, band=4, stripes=0, strength=12.0, q_dir=False),
+    budgets_sweep=(1.0, 0.3), taus_sweep=(2.0, 4.0, 6.0, 8.0),
+)
+
 # Test-only variant of the tiny case with a strong sink so that the in-kernel
 # skip actually fires (sink logit around 16 nats); not a benchmark workload.
 TINY_SKIP = TINY.with_(
@@ -134,7 +144,7 @@ TINY_SKIP = TINY.with_(
 )
 
 WORKLOADS: Dict[str, Workload] = {
-    w.name: w for w in (TINY, LLAMA_32K, LLAMA_128K, QWEN_128K, STRESS, TINY_SKIP)
+    w.name: w for w in (TINY, LLAMA_32K, LLAMA_128K, QWEN_128K, STRESS, REMAP_32K, TINY_SKIP)
 }
 
 

@@ -230,6 +230,25 @@ cosa_status cosa_osk_prefill_delta(const cosa_problem* p, const void* q, const v
 cosa_status cosa_dense_prefill(const cosa_problem* p, const void* q, const void* k_pool,
                                const void* v_pool, void* out, float* lse, void* stream);
 
+/*
+ * Logical mask skipping on the same kernel, the comparison point of the
+ * kernel microbenchmark of CoSA (paperpeel) App. D.3, Fig. B (and §4.3): a
+ * block-sparse kernel driven by a binary block mask walks every causal block
+ * of a tile in ascending order and computes only the selected ones, paying
+ * the loop control and the per-block workgroup barrier on the unselected
+ * ones too, whereas the OSK jumps straight to the pages of its ordered list.
+ * No in-kernel skip.
+ *
+ * block_mask  device uint32 [rows][mask_words]: bit (j % 32) of word j / 32
+ *             of mask row (b, h, i) selects causal key block j of that tile;
+ *             bits at or past the tile's causal block count are ignored.
+ * mask_words  >= ceil(ceil(max_seqlen / kv_block) / 32).
+ * out / lse as for cosa_osk_prefill(), over the selected blocks.
+ */
+cosa_status cosa_block_mask_prefill(const cosa_problem* p, const void* q, const void* k_pool,
+                                    const void* v_pool, const uint32_t* block_mask,
+                                    int64_t mask_words, void* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

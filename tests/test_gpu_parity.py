@@ -339,3 +339,63 @@ def test_kap_top_p_matches_oracle(case):
     assert exact > 0 and ties <= max(1, exact // 100)
     if top_p < 1.0:
         assert shorter > 0
+
+
+# ---------------------------------------------------------------------------
+# Remapping ablation and logical mask skipping
+
+
+def test_osk_ascending_order_of_kap_set_with_skip():
+    # the KAP kept sets visited in ascending block order (no remapping), skip on
+    w, x = _inputs("tiny_skip")
+    print("[case] osk ascending kap set tau=4", flush=True)
+    m = okap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
+                                w.q_block, w.page_size, w.budget, w.softmax_scale)
+    asc = m.blocks.copy()
+    for idx in np.ndindex(*m.counts.shape):
+        c = m.counts[idx]
+        asc[idx][:c] = np.sort(asc[idx][:c])
+    _run_osk_vs_oracle(w, x, asc, m.counts, 4.0, "osk ascending tau=4")
+
+
+@pytest.mark.parametrize("case", [("tiny", dict(RAGGED), 0.3), ("tiny_skip", {}, 0.2),
+                                  ("tiny", dict(RAGGED, q_block=64, head_dim=64), 0.5)])
+def test_block_mask_logical_skip_matches_oracle(case):
+    from block_sparse_long_kap_amd.masks import block_bitmask
+    name, kw, budget = case
+    w, x = _inputs(name, **kw)
+    print(f"[case] logical skip {name} {kw} budget={budget}", flush=True)
+    prob, q, k, v = upload(x, DEV)
+    gm = bk.proxy_ordered_mask(prob, q, k, budget)
+    bits = block_bitmask(prob, gm)
+    res = bk.block_mask_prefill(prob, q, k, v, bits)
+    osk = bk.osk_prefill(prob, q, k, v, gm, -1.0)
+    torch.cuda.synchronize()
+    out, lse = _np(res.out), _np(res.lse)
+    gb, gc = _np(gm.blocks), _np(gm.counts)
+    st, ls = ErrStats(), ErrStats()
+    grp = w.num_q_heads // w.num_kv_heads
+    for b in range(w.batch):
+        s0, L = int(x.cu_seqlens[b]), int(x.seqlens[b])
+        if L == 0:
+            continue
+        kk = materialise(x.k_pool, x.page_table[b], L, w.page_size)
+        vv = materialise(x.v_pool, x.page_table[b], L, w.page_size)
+        for h in range(w.num_q_heads):
+            for i in range((L + w.q_block - 1) // w.q_block):
+                rows = np.arange(i * w.q_block, min((i + 1) * w.q_block, L))
+                key_ok = np.zeros(L, dtype=bool)
+                for j in gb[b, h, i, :gc[b, h, i]]:
+                    key_ok[j * w.page_size:min((j + 1) * w.page_size, L)] = True
+                o, l_ = odense.attention_rows(x.q[s0 + rows, h].astype(np.float64), rows,
+                                              kk[:, h // grp], vv[:, h // grp], w.softmax_scale,
+                                              key_ok=key_ok)
+                st.add(out[s0 + rows, h], o)
+                fin = np.isfinite(l_)
+                assert np.array_equal(np.isfinite(lse[h, s0 + rows]), fin)
+                ls.add(lse[h, s0 + rows][fin], l_[fin])
+    st.assert_ok(label=f"logical skip {name} out")
+    ls.assert_ok(max_abs=1e-3, mean_abs=1e-4, label=f"logical skip {name} lse")
+    # the same set through the OSK (skip off) agrees with it to rounding order
+    d = np.abs(_np(osk.out).astype(np.float64) - out)
+    assert d.max() <= 2e-2
