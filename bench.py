@@ -214,7 +214,7 @@ def main():
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
                      "traffic_unit": "bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1)",
                      "traffic_source": None if traffic is None else TRAFFIC_PROFILE,
-                     "kernel": "attn_fwd_kernel<128,4,ordered> (cosa_osk_prefill)",
+                     "kernel": "attn_fwd_kernel<128, 4, 1> (cosa_osk_prefill)",
                      "algorithmic_flop_per_launch": osk_flops},
         "cpu_baseline": None,
     }

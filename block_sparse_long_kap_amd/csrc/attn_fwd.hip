@@ -20,14 +20,14 @@
 //     of the 64 keys of a page, so the row max is an in-register reduction
 //     plus one exchange with the partner lane (lane ^ 32).
 //   * The value product is O^T = V^T P^T on the same MFMA: P^T comes straight
-//     from the S^T accumulator registers (rounded to bf16) and the page's V is
-//     staged transposed in LDS, in the key order the accumulator layout
+//     from the S^T accumulator registers (rounded to bf16); the V^T operand
+//     is read from the page as stored ([key][D]) with the gfx950 transposing
+//     LDS read (ds_read_b64_tr_b16), in the key order the accumulator layout
 //     implies.
-//   * K and V^T pages are double-buffered in LDS.  K pages are copied from
-//     HBM straight into LDS two pages ahead; the next V page is loaded into
-//     registers while the current page is computed and transposed into LDS
-//     at the start of the next step.  One workgroup barrier per visited page
-//     carries both the LDS hand-off and the tile-wide skip vote.
+//   * K and V pages are double-buffered in LDS and copied from HBM straight
+//     into LDS (no registers): K two pages ahead, V one page ahead.  One
+//     workgroup barrier per visited page carries both the LDS hand-off and
+//     the tile-wide skip vote.
 //   * Tile order: one (sequence, KV head) group at a time over the whole
 //     chip, longest tiles (most causal blocks) first inside the group, so the
 //     working set is that group's pages.  A level-major order and one that
@@ -46,6 +46,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -56,27 +57,26 @@ __device__ __forceinline__ float pair_max(float x) {
 }
 __device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
 
-// K page in LDS: [64 keys][D] bf16 with 16-byte chunks XOR-swizzled by the
-// row, so that the 16-byte operand reads of consecutive key rows land in
-// distinct banks.  Pages are copied HBM -> LDS directly (no registers): lane
-// i of a copy instruction writes the i-th 16-byte slot of its wavefront's
-// span, and fetches whichever logical chunk belongs in that slot.
+// K and V pages in LDS: [64 keys][D] bf16 as in HBM, with the 16-byte
+// chunks of each row permuted by a function of the row.  Pages are copied
+// HBM -> LDS directly (no registers): lane i of a copy instruction writes the
+// i-th 16-byte slot of its wavefront's span and fetches whichever logical
+// chunk belongs in that slot.  The permutation (swap of the two 2-bit halves
+// of row mod 16, for D = 128) spreads both access patterns over the banks:
+// the QK operand reads (32 consecutive rows, one chunk) and the transposed
+// P V operand reads (8 rows x 4 chunks per instruction).
 template <int D>
-struct KLayout {
+struct PageLayout {
   static constexpr int kChunks = D / 8;
-  static constexpr int kSwz = (kChunks < 16 ? kChunks : 16) - 1;
   static constexpr int kBytes = kPage * D * 2;
-  static __device__ __forceinline__ int offset(int row, int chunk16) {
-    return row * (D * 2) + ((chunk16 ^ (row & kSwz)) << 4);
+  static __device__ __forceinline__ int swz(int row) {
+    if constexpr (kChunks >= 16)
+      return ((row & 3) << 2) | ((row >> 2) & 3);
+    else
+      return ((row & 3) << 1) | ((row >> 2) & 1);
   }
-};
-// V^T page in LDS: [D][64 keys] bf16, rows padded by 8 bytes so that the 32
-// rows one operand read touches fall into distinct banks while every read of a
-// wavefront stays "one base register + immediate offset".
-struct VLayout {
-  static constexpr int kStride = kPage * 2 + 8;
-  static __device__ __forceinline__ int offset(int d, int chunk8) {
-    return d * kStride + chunk8 * 8;
+  static __device__ __forceinline__ int offset(int row, int chunk16) {
+    return row * (D * 2) + ((chunk16 ^ swz(row)) << 4);
   }
 };
 
@@ -97,6 +97,21 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, int bid, int& b
     const int gi = rem / hg;
     const int hh = rem - gi * hg;
     const int G = x + 8 * gi;
+    b = G / p.hkv;
+    const int g = G - b * p.hkv;
+    h = g * hg + hh;
+    i = p.nqb - 1 - level;
+  } else if (p.order == kOrderGroupXcd) {
+    // group-major sequence of (group, level) units, each unit's hg query
+    // heads on one XCD (workgroup ids go round-robin over the 8 XCDs): unit u
+    // runs on XCD u % 8, each XCD takes its units in sequence order, so the
+    // heads that share the group's pages share that XCD's L2
+    const int x = bid & 7;
+    const int r = bid >> 3;
+    const int unit = (r / hg) * 8 + x;
+    const int hh = r - (r / hg) * hg;
+    const int G = unit / p.nqb;
+    const int level = unit - G * p.nqb;
     b = G / p.hkv;
     const int g = G - b * p.hkv;
     h = g * hg + hh;
@@ -131,11 +146,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   constexpr int NT = NW * 64;
   constexpr int BQ = NW * 32;
   constexpr int KCH = D / 8;                         // 16-byte chunks per key row
-  constexpr int K_TOTAL = kPage * KCH;               // 16-byte chunks per K page
-  static_assert(K_TOTAL % NT == 0, "K page copy must split evenly over the workgroup");
+  constexpr int K_TOTAL = kPage * KCH;               // 16-byte chunks per page
+  static_assert(K_TOTAL % NT == 0, "page copy must split evenly over the workgroup");
   constexpr int K_PER = K_TOTAL / NT;
-  constexpr int V_TOTAL = KCH * (kPage / 4);         // (key-quad, d-chunk) pairs
-  constexpr int V_PER = (V_TOTAL + NT - 1) / NT;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   // Lazy rescaling: the reference max used for the exponentials only moves
@@ -146,10 +159,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   // Two buffers per operand as distinct LDS objects, so that the compiler
   // can tell reads of one buffer from the asynchronous HBM->LDS copies into
   // the other and does not wait for those copies before the reads.
-  __shared__ __attribute__((aligned(16))) unsigned char sK0[KLayout<D>::kBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char sK1[KLayout<D>::kBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char sV0[D * VLayout::kStride];
-  __shared__ __attribute__((aligned(16))) unsigned char sV1[D * VLayout::kStride];
+  __shared__ __attribute__((aligned(16))) unsigned char sK0[PageLayout<D>::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sK1[PageLayout<D>::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sV0[PageLayout<D>::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sV1[PageLayout<D>::kBytes];
   __shared__ int sVote[2][NW];
   __shared__ int sSlot[2][2][64];   // [page | block][ring chunk][slot]
   // logical-skip mode: the tile's block bitmask (up to 16384 causal blocks)
@@ -217,8 +230,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
 
   // Slot -> (logical block, page) lookups come from a two-chunk ring of 64
   // entries in LDS (uniform-address reads, no vector-memory wait on the page
-  // loop).  Wave 0 fetches chunk c+1 from memory when slot 64c starts and
-  // writes it into the ring one page later, long before it is read.
+  // loop).  When slot 64c starts, wave 0 copies chunk c+1 from memory straight
+  // into the ring half that chunk c-1 used (HBM -> LDS); it is read 62 slots
+  // and as many barriers later.
   const int32_t* __restrict__ page_src = kOrdered ? op : pt;
   auto chunk_entry = [&](const int32_t* src, int c) -> int {
     const int t = c * 64 + lane;
@@ -232,7 +246,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     }
   }
   __syncthreads();   // every wave reads the ring (and bitmask) just filled
-  int pend_pg = 0, pend_bl = 0, pend_chunk = -1;
   auto slot_page = [&](int t) -> int {
     return __builtin_amdgcn_readfirstlane(sSlot[0][(t >> 6) & 1][t & 63]);
   };
@@ -240,92 +253,41 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     return kOrdered ? __builtin_amdgcn_readfirstlane(sSlot[1][(t >> 6) & 1][t & 63]) : t;
   };
   auto advance_chunks = [&](int t_next) {
-    if (pend_chunk >= 0) {   // fetched one page ago: the barrier since has waited for it
-      if (wave == 0) {
-        sSlot[0][pend_chunk & 1][lane] = pend_pg;
-        if (kOrdered) sSlot[1][pend_chunk & 1][lane] = pend_bl;
-      }
-      pend_chunk = -1;
-    }
-    if ((t_next & 63) == 0 && t_next > 0 && ((t_next >> 6) + 1) * 64 < cnt) {
-      pend_chunk = (t_next >> 6) + 1;
-      if (wave == 0) {
-        pend_pg = chunk_entry(page_src, pend_chunk);
-        if (kOrdered) pend_bl = chunk_entry(ob, pend_chunk);
-      }
+    if (wave == 0 && (t_next & 63) == 0 && t_next > 0 && ((t_next >> 6) + 1) * 64 < cnt) {
+      const int c = (t_next >> 6) + 1;
+      const int t = min(c * 64 + lane, cnt - 1);   // lanes past the count re-read a valid entry
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(page_src + t),
+                                       (__attribute__((address_space(3))) void*)&sSlot[0][c & 1][0],
+                                       4, 0, 0);
+      if (kOrdered)
+        __builtin_amdgcn_global_load_lds(
+            static_cast<const void*>(ob + t),
+            (__attribute__((address_space(3))) void*)&sSlot[1][c & 1][0], 4, 0, 0);
+      // once per 64 slots: keeps any ring copy from being outstanding across
+      // the loop back-edge, where the compiler would wait for it (and for the
+      // page prefetches) before every QK
+      __builtin_amdgcn_s_waitcnt(0);
     }
   };
   const int64_t head_stride = (int64_t)kPage * D;              // elements per (page, head)
   const int64_t page_stride = (int64_t)p.hkv * head_stride;
 
-  // ---- K: HBM -> LDS without registers (16 bytes per lane per instruction)
-  auto copy_k = [&](int page, int buf) {
-    unsigned char* kb = kbuf(buf);
-    const uint16_t* base = p.k_pool + (int64_t)page * page_stride + (int64_t)g * head_stride;
+  // ---- K and V pages: HBM -> LDS without registers (16 bytes per lane per
+  // instruction)
+  auto copy_page = [&](const uint16_t* pool, int page, unsigned char* dst) {
+    const uint16_t* base = pool + (int64_t)page * page_stride + (int64_t)g * head_stride;
 #pragma unroll
     for (int e = 0; e < K_PER; ++e) {
       const int f = e * NT + tid;              // physical 16-byte slot in the page
       const int r = f / KCH;
-      const int c = (f % KCH) ^ (r & KLayout<D>::kSwz);
+      const int c = (f % KCH) ^ PageLayout<D>::swz(r);
       __builtin_amdgcn_global_load_lds(
           static_cast<const void*>(base + r * D + c * 8),
-          (__attribute__((address_space(3))) void*)(kb + (e * NT + wave * 64) * 16),
-          16, 0, 0);
+          (__attribute__((address_space(3))) void*)(dst + (e * NT + wave * 64) * 16), 16, 0, 0);
     }
   };
-
-  // ---- V: HBM -> registers -> transposed into LDS.  Pair idx covers keys
-  // 4kq..4kq+3 and dims 8c..8c+7; key-quads vary fastest across lanes so the
-  // transposed LDS writes of 16 lanes fill one V^T row without bank conflicts.
-  u32x4_t vreg[V_PER][4];
-  auto load_v = [&](int page) {
-    const uint16_t* base = p.v_pool + (int64_t)page * page_stride + (int64_t)g * head_stride;
-#pragma unroll
-    for (int e = 0; e < V_PER; ++e) {
-      const int idx = tid + e * NT;
-      if (V_TOTAL % NT == 0 || idx < V_TOTAL) {
-        const int kq = idx % (kPage / 4), c = idx / (kPage / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vreg[e][r] = *reinterpret_cast<const u32x4_t*>(base + (kq * 4 + r) * D + c * 8);
-      }
-    }
-  };
-  auto store_v = [&](int buf, int block) {
-    unsigned char* vb = vbuf_of(buf);
-    const bool tail = block * kPage + kPage > L;     // uniform
-    const int valid_keys = L - block * kPage;
-#pragma unroll
-    for (int e = 0; e < V_PER; ++e) {
-      const int idx = tid + e * NT;
-      if (V_TOTAL % NT == 0 || idx < V_TOTAL) {
-        const int kq = idx % (kPage / 4), c = idx / (kPage / 4);
-        if (tail) {
-          // unused slots of a sequence's last page may hold anything: zero them
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool ok = kq * 4 + r < valid_keys;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) vreg[e][r][w] = ok ? vreg[e][r][w] : 0u;
-          }
-        }
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // dims 2w (low halves) and 2w+1 (high halves) of keys 4kq..4kq+3
-          const uint32_t a0 = vreg[e][0][w], a1 = vreg[e][1][w];
-          const uint32_t a2 = vreg[e][2][w], a3 = vreg[e][3][w];
-          u32x2_t lo, hi;
-          lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-          lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-          hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-          hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-          const int d = c * 8 + 2 * w;
-          *reinterpret_cast<u32x2_t*>(vb + VLayout::offset(d, kq)) = lo;
-          *reinterpret_cast<u32x2_t*>(vb + VLayout::offset(d + 1, kq)) = hi;
-        }
-      }
-    }
-  };
+  auto copy_k = [&](int page, int buf) { copy_page(p.k_pool, page, kbuf(buf)); };
+  auto copy_v = [&](int page, int buf) { copy_page(p.v_pool, page, vbuf_of(buf)); };
 
   f32x16_t o[DBLK];
 #pragma unroll
@@ -348,7 +310,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-            kb + KLayout<D>::offset(mb * 32 + col, 2 * ks + hf));
+            kb + PageLayout<D>::offset(mb * 32 + col, 2 * ks + hf));
         sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, a), qf[ks], ks == 0 ? (f32x16_t){} : sacc[mb], 0, 0,
             0);
@@ -369,25 +331,51 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     }
     return part;
   };
-  // O^T += V^T P^T
+  // O^T += V^T P^T.  The A operand (V^T: 32 dims x 16 keys per lane block)
+  // comes from the [key][D] page with ds_read_b64_tr_b16: in each group of 16
+  // lanes, lane 4k+q reads 4 dims (4q..4q+3 of the group's 16) of key row k,
+  // and the transposed result gives lane i those 4 keys of dim i.  Keys of a
+  // lane's operand follow the S^T accumulator order: 16ks + 8r + 4hf + 0..3
+  // for the two reads r.  Read offsets per (r, dim block); ks adds 16 rows.
+  int vtr[2][DBLK];
+  {
+    const int tr_row = 4 * hf + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = 8 * r + tr_row;
+#pragma unroll
+      for (int md = 0; md < DBLK; ++md) {
+        const int colx = md * 32 + tr_col;
+        vtr[r][md] = PageLayout<D>::offset(row, colx >> 3) + ((colx & 7) << 1);
+      }
+    }
+  }
   auto pv = [&](const unsigned char* vb, const bf16x8_t (&pb)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int md = 0; md < DBLK; ++md) {
-        const int d = md * 32 + col;
         u32x4_t a;
-        const u32x2_t a0 = *reinterpret_cast<const u32x2_t*>(vb + VLayout::offset(d, 4 * ks + hf));
-        const u32x2_t a1 =
-            *reinterpret_cast<const u32x2_t*>(vb + VLayout::offset(d, 4 * ks + 2 + hf));
-        a[0] = a0[0];
-        a[1] = a0[1];
-        a[2] = a1[0];
-        a[3] = a1[1];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16_t*)(vb + vtr[r][md] + ks * (32 * D)));
+          const u32x2_t w = __builtin_bit_cast(u32x2_t, v);
+          a[2 * r] = w[0];
+          a[2 * r + 1] = w[1];
+        }
         o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb[ks],
                                                         o[md], 0, 0, 0);
       }
     }
+  };
+  // Key rows past the end of the sequence on its last page may hold anything
+  // (P is 0 there, but 0 * NaN is not): zero them in the V page before P V.
+  auto zero_v_tail = [&](unsigned char* vb, int valid_keys) {
+    constexpr int kRowChunks = D / 8;
+    for (int f = valid_keys * kRowChunks + tid; f < kPage * kRowChunks; f += NT)
+      *reinterpret_cast<u32x4_t*>(vb + f * 16) = (u32x4_t){0u, 0u, 0u, 0u};
   };
   // causal / end-of-sequence mask (diagonal and tail pages only), then the
   // row's block max in log2 units
@@ -419,10 +407,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   };
 
   // Page loop, one workgroup barrier per visited page.  Iteration t: S(t)
-  // from the K page already in LDS, mask, block max and the tile vote; V(t)
-  // (fetched during the previous page) to LDS; barrier; read the vote; start
-  // the copies of K(t+2) (HBM -> LDS) and V(t+1) (HBM -> registers); then the
-  // softmax and P V of page t unless the tile skips it.
+  // from the K page already in LDS, mask, block max and the tile vote;
+  // barrier (every copy issued so far has landed); read the vote; start the
+  // copies of K(t+2) and V(t+1) (HBM -> LDS); then the softmax and P V of
+  // page t unless the tile skips it.
   int j_cur = 0, j_next = 0;
   if (cnt > 0) {
     j_cur = slot_block(0);
@@ -431,12 +419,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       j_next = slot_block(1);
       if (selected(1)) copy_k(slot_page(1), 1);
     }
-    if (selected(0)) load_v(slot_page(0));
+    if (selected(0)) copy_v(slot_page(0), 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   for (int t = 0; t < cnt; ++t) {
-    advance_chunks(t + 1);   // chunk holding slot t+1 (and t+2) is current
     const int buf = t & 1;
     const int key0 = j_cur * kPage;
     const bool sel = selected(t);
@@ -449,7 +436,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       bm = mask_max(j_cur, sacc);
     }
     vote(bm, buf);
-    if (sel) store_v(buf, j_cur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -465,14 +451,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       if (p.skip_record != nullptr && tid == 0) p.skip_record[row * p.capacity + t] = skip ? 1 : 0;
     }
 
-    // ---- prefetch: K(t+2) straight into LDS, V(t+1) into registers
+    // ---- prefetch: K(t+2) and V(t+1) straight into LDS, and the slot chunk
+    // after the one that holds slot t+1
+    advance_chunks(t + 1);
     const int j_after = j_next;
     if (t + 2 < cnt) {
       j_next = slot_block(t + 2);
       if (selected(t + 2)) copy_k(slot_page(t + 2), buf);
     }
-    if (t + 1 < cnt && selected(t + 1)) load_v(slot_page(t + 1));
+    if (t + 1 < cnt && selected(t + 1)) copy_v(slot_page(t + 1), buf ^ 1);
 
+    if (sel && !skip && key0 + kPage > L) {   // uniform: the sequence's last page
+      zero_v_tail(vbuf_of(buf), L - key0);
+      __syncthreads();
+    }
     if (active && !skip) {
       // ---- online softmax (log2 domain) with lazy rescaling
       const float mn = fmaxf(m_true, bm);

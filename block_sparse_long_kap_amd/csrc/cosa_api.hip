@@ -103,11 +103,16 @@ void fill_attn(cosa::AttnParams& a, const cosa_problem* p, const void* q, const 
   a.max_pages = p->max_pages_per_seq;
   a.nqb = (int32_t)ceil_div(p->max_seqlen, p->q_block);
   a.xcd_groups = xcd_groups(p);
+  {
+    const int64_t units = (int64_t)p->batch * p->num_kv_heads * a.nqb;
+    a.xcd_units = units % 8 == 0 ? (int32_t)units : 0;
+  }
 #ifndef COSA_TILE_ORDER
 #define COSA_TILE_ORDER cosa::kOrderGroupMajor
 #endif
   a.order = COSA_TILE_ORDER;
   if (a.order == cosa::kOrderXcdGroup && a.xcd_groups == 0) a.order = cosa::kOrderLevel;
+  if (a.order == cosa::kOrderGroupXcd && a.xcd_units == 0) a.order = cosa::kOrderGroupMajor;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   a.skip_mode = cosa::kSkipOff;
   a.tau_log2 = 0.f;

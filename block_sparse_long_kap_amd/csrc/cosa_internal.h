@@ -15,7 +15,9 @@ constexpr int kMaxCandidates = 2048;  // KAP: key blocks per tile handled in one
 enum TileOrder : int32_t {
   kOrderLevel = 0,      // tile level major, every head of the batch per level
   kOrderXcdGroup = 1,   // every KV group pinned to one XCD (needs B*Hkv % 8 == 0)
-  kOrderGroupMajor = 2  // one KV group after the other: its K/V stay cache-resident
+  kOrderGroupMajor = 2, // one KV group after the other: its K/V stay cache-resident
+  kOrderGroupXcd = 3    // group-major, the query heads of one (group, tile) on one XCD
+                        // (needs B*Hkv*NQB % 8 == 0)
 };
 
 // Arguments of the attention kernel (dense and ordered-skipping modes).
@@ -38,6 +40,7 @@ struct AttnParams {
   int64_t total_q;
   int32_t batch, hq, hkv, max_pages, nqb;
   int32_t xcd_groups;             // B*Hkv when it is a multiple of 8, else 0
+  int32_t xcd_units;              // B*Hkv*NQB when it is a multiple of 8, else 0
   int32_t order;                  // tile order, one of TileOrder
   float scale_log2;               // softmax_scale * log2(e)
   int32_t skip_mode;              // OSK: kSkipOff, kSkipTau or kSkipDelta

@@ -51,6 +51,17 @@ def attention_source_digest(read=None) -> str:
     return h.hexdigest()[:16]
 
 
+def entry_of(kernel: str):
+    """C entry point that launches an attention kernel instance, from the last
+    template argument (the page-walk mode), or None for other kernels."""
+    m = re.search(r"attn_fwd_kernel<\s*\d+,\s*\d+,\s*(\w+)\s*>", kernel)
+    if not m:
+        return None
+    return {"0": "cosa_dense_prefill", "false": "cosa_dense_prefill",
+            "1": "cosa_osk_prefill", "true": "cosa_osk_prefill",
+            "2": "cosa_block_mask_prefill"}.get(m.group(1))
+
+
 def short_name(kernel: str) -> str:
     s = kernel
     if "::" in s:
@@ -113,7 +124,8 @@ def traffic_md(fetch, write, cfetch, cwrite, copy_bytes, workload, budget, tau, 
         lines.append(f"| `{short_name(k)}` | {len(v)} | {fk:.6g} | {wk:.6g} | {rd / 1e9:.3f} | "
                      f"{wt / 1e9:.3f} | {(rd + wt) / 1e9:.3f} |")
         if "attn_fwd_kernel" in k:
-            records.append({"kernel": short_name(k), "workload": workload, "budget": budget,
+            records.append({"kernel": short_name(k), "entry": entry_of(k),
+                            "workload": workload, "budget": budget,
                             "tau": tau, "read_bytes": round(rd), "write_bytes": round(wt),
                             "bytes_per_launch": round(rd + wt), "source_digest": digest})
     lines.append("")
@@ -151,7 +163,7 @@ def read_traffic(path, workload, budget, tau):
             if not line.startswith("bench-traffic: "):
                 continue
             r = json.loads(line[len("bench-traffic: "):])
-            if ("true" in r["kernel"] and r["workload"] == workload and
+            if (r.get("entry") == "cosa_osk_prefill" and r["workload"] == workload and
                     abs(r["budget"] - budget) < 1e-9 and abs(r["tau"] - tau) < 1e-9 and
                     r["source_digest"] == digest):
                 return r

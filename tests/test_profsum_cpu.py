@@ -23,7 +23,7 @@ def _counter_csv(path, rows):
 
 
 def test_traffic_scaling_and_readback(tmp_path):
-    attn = "void cosa::(anonymous namespace)::attn_fwd_kernel<128, 4, true>(cosa::AttnParams)"
+    attn = "void cosa::(anonymous namespace)::attn_fwd_kernel<128, 4, 1>(cosa::AttnParams)"
     _counter_csv(tmp_path / "f.csv", [(attn, "FETCH_SIZE", 100.0), (attn, "FETCH_SIZE", 300.0)])
     _counter_csv(tmp_path / "w.csv", [(attn, "WRITE_SIZE", 50.0)])
     _counter_csv(tmp_path / "cf.csv", [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 512.0)])
@@ -49,3 +49,11 @@ def test_committed_profile_parses():
     assert os.path.exists(path)
     with open(path) as f:
         assert any(line.startswith("bench-traffic: ") for line in f)
+
+
+def test_entry_points_from_kernel_names():
+    k = "void cosa::(anonymous namespace)::attn_fwd_kernel<128, 4, {}>(cosa::AttnParams)"
+    assert profsum.entry_of(k.format(1)) == "cosa_osk_prefill"
+    assert profsum.entry_of(k.format(0)) == "cosa_dense_prefill"
+    assert profsum.entry_of(k.format(2)) == "cosa_block_mask_prefill"
+    assert profsum.entry_of("void cosa::(anonymous namespace)::kap_select<128, 8, false>(x)") is None
