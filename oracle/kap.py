@@ -32,6 +32,10 @@ the reading taken here:
   ``beta_ppm = floor(beta * 1e6 + 0.5)``; truncation happens after the two
   groups are concatenated, so an HRM block can displace a higher-w non-HRM
   block.
+* KV-group-shared masks (one mask for the query heads that share a KV head,
+  the GQA packing the pages leave to the implementation): the proxy rows of
+  all the group's heads for the tile are scored together, w_j is their mean
+  and HRM marks the arg-max block of any of them; the rest is unchanged.
 * Top-p (§5.1 "Hyperparameters", App. D.1: stage-1 Top-p with p = 0.95):
   the importance scores of a tile sum to 1 (each proxy row's softmax sums to
   1 over its candidates), so they are read as the probability mass of the
@@ -187,6 +191,23 @@ def head_tiles(q_h: np.ndarray, k_g: np.ndarray, scale: float, q_block: int,
                         beta_ppm, top_p) for i in idx}
 
 
+def group_tiles(q_heads, k_g: np.ndarray, scale: float, q_block: int, kv_block: int,
+                beta_ppm: int, rows_per_proxy: int = ROWS_PER_PROXY, tiles=None, top_p=None):
+    """KAP for every tile (or the listed tiles) of one (sequence, KV head) with
+    one mask shared by the group's query heads ``q_heads`` (a list of [L][D]
+    arrays): the proxy rows of every head for the tile are scored together."""
+    kbar = pooled_keys(k_g, kv_block)
+    pooled = [pooled_queries(qh, q_block, rows_per_proxy) for qh in q_heads]
+    nqb = pooled[0][0].shape[0]
+    idx = range(nqb) if tiles is None else tiles
+    out = {}
+    for i in idx:
+        qbar = np.concatenate([qb[i][va[i]] for qb, _, va in pooled], axis=0)
+        last = np.concatenate([la[i][va[i]] for _, la, va in pooled], axis=0)
+        out[i] = kap_tile(qbar, last, kbar, scale, kv_block, beta_ppm, top_p)
+    return out
+
+
 @dataclass
 class OrderedMask:
     blocks: np.ndarray      # int32 [B][Hq][NQBmax][C], -1 past count
@@ -200,13 +221,15 @@ class OrderedMask:
 def proxy_ordered_mask(q: np.ndarray, k_pool: np.ndarray, page_table: np.ndarray,
                        cu_seqlens: np.ndarray, num_kv_heads: int, q_block: int,
                        kv_block: int, budget: float, scale: float,
-                       rows_per_proxy: int = ROWS_PER_PROXY, top_p=None) -> OrderedMask:
+                       rows_per_proxy: int = ROWS_PER_PROXY, top_p=None,
+                       shared_kv: bool = False) -> OrderedMask:
     """M_KAP for a packed batch, in the layout of the C ABI.
 
     q [T][Hq][D], k_pool [P][Hkv][page][D] (bf16-exact values, any float
     dtype), page_table [B][max_pages], cu_seqlens [B+1].  With ``top_p`` the
     kept count is the smaller of the budget count and the Top-p count; the
-    capacity stays the budget's.
+    capacity stays the budget's.  With ``shared_kv`` there is one mask row
+    per (sequence, KV head, tile): arrays are [B][Hkv][NQBmax](...).
     """
     T, Hq, D = q.shape
     grp = Hq // num_kv_heads
@@ -215,10 +238,11 @@ def proxy_ordered_mask(q: np.ndarray, k_pool: np.ndarray, page_table: np.ndarray
     max_len = int(np.max(np.diff(cu_seqlens))) if B > 0 else 0
     nqb_max = max((max_len + q_block - 1) // q_block, 1)
     C = mask_capacity(max_len, kv_block, beta_ppm)
-    blocks = np.full((B, Hq, nqb_max, C), -1, dtype=np.int32)
-    pages = np.full((B, Hq, nqb_max, C), -1, dtype=np.int32)
-    counts = np.zeros((B, Hq, nqb_max), dtype=np.int32)
-    hrm_counts = np.zeros((B, Hq, nqb_max), dtype=np.int32)
+    H = num_kv_heads if shared_kv else Hq
+    blocks = np.full((B, H, nqb_max, C), -1, dtype=np.int32)
+    pages = np.full((B, H, nqb_max, C), -1, dtype=np.int32)
+    counts = np.zeros((B, H, nqb_max), dtype=np.int32)
+    hrm_counts = np.zeros((B, H, nqb_max), dtype=np.int32)
     tiles = {}
     page_size = k_pool.shape[2]
     if page_size != kv_block:
@@ -227,11 +251,16 @@ def proxy_ordered_mask(q: np.ndarray, k_pool: np.ndarray, page_table: np.ndarray
         if L == 0:
             continue
         keys = materialise(k_pool, page_table[b], L, page_size)        # [L][Hkv][D]
-        for h in range(Hq):
-            g = h // grp
-            res = head_tiles(np.asarray(q[start:start + L, h, :], dtype=np.float64),
-                             keys[:, g, :], scale, q_block, kv_block, beta_ppm,
-                             rows_per_proxy, top_p=top_p)
+        for h in range(H):
+            if shared_kv:
+                res = group_tiles([np.asarray(q[start:start + L, hh, :], dtype=np.float64)
+                                   for hh in range(h * grp, (h + 1) * grp)],
+                                  keys[:, h, :], scale, q_block, kv_block, beta_ppm,
+                                  rows_per_proxy, top_p=top_p)
+            else:
+                res = head_tiles(np.asarray(q[start:start + L, h, :], dtype=np.float64),
+                                 keys[:, h // grp, :], scale, q_block, kv_block, beta_ppm,
+                                 rows_per_proxy, top_p=top_p)
             for i, tp in res.items():
                 kk = tp.k
                 blocks[b, h, i, :kk] = tp.blocks

@@ -218,3 +218,66 @@ def test_top_p_invariants_on_random_tiles():
             if prev is not None:
                 assert np.all(ks >= prev)
             prev = ks
+
+
+# ---------------------------------------------------------------------------
+# KV-group-shared masks (one mask per KV head for its query heads)
+
+
+def test_gqa_shared_golden():
+    ex = _golden()["gqa_shared"]
+    L, kb = ex["L"], ex["kv_block"]
+    k = np.zeros((L, ex["D"]))
+    for j, vec in enumerate(ex["block_key"]):
+        k[j * kb:(j + 1) * kb] = vec
+    qs = [np.tile(np.asarray(v, dtype=np.float64), (L, 1)) for v in ex["head_query"]]
+    beta = kap.budget_ppm(ex["budget"])
+    t = kap.group_tiles(qs, k, ex["scale"], ex["q_block"], kb, beta, ex["rows_per_proxy"])[0]
+    assert np.allclose(t.w, ex["expect_w"], rtol=0, atol=1e-15)
+    assert list(t.hrm) == ex["expect_hrm"]
+    assert list(t.order) == ex["expect_order"]
+    assert list(t.blocks) == ex["expect_blocks"]
+    for qh, want in zip(qs, ex["expect_per_head_blocks"]):
+        alone = kap.head_tiles(qh, k, ex["scale"], ex["q_block"], kb, beta, ex["rows_per_proxy"])[0]
+        assert list(alone.blocks) == want
+
+
+def test_gqa_shared_brute_force_importance():
+    """w_j of the shared mask is the mean over every head's proxy rows of that
+    row's softmax over its own candidates, written out with loops."""
+    rng = np.random.default_rng(7)
+    L, D, qb, kb, g = 150, 3, 64, 16, 16
+    qs = [rng.standard_normal((L, D)) for _ in range(3)]
+    k = rng.standard_normal((L, D))
+    scale = 0.6
+    res = kap.group_tiles(qs, k, scale, qb, kb, kap.budget_ppm(1.0), g)
+    for i, t in res.items():
+        rows = []
+        for qh in qs:
+            for r in range(qb // g):
+                pos = [x for x in range(i * qb + r * g, i * qb + (r + 1) * g) if x < L]
+                if not pos:
+                    continue
+                qbar = [sum(qh[x, d] for x in pos) / len(pos) for d in range(D)]
+                cand = pos[-1] // kb + 1
+                kbar = [[sum(k[u, d] for u in range(j * kb, min((j + 1) * kb, L))) /
+                         (min((j + 1) * kb, L) - j * kb) for d in range(D)] for j in range(cand)]
+                sc = [scale * sum(qbar[d] * kbar[j][d] for d in range(D)) for j in range(cand)]
+                mx = max(sc)
+                z = math.fsum(math.exp(v - mx) for v in sc)
+                rows.append([math.exp(v - mx) / z for v in sc] + [0.0] * (t.n - cand))
+        w = np.mean(np.asarray(rows), axis=0)
+        assert np.allclose(t.w, w, atol=1e-12)
+
+
+def test_gqa_shared_equals_per_head_for_one_head_groups():
+    x = ci.make(ci.get("tiny"))
+    w_ = x.workload
+    a = kap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w_.num_kv_heads,
+                               w_.q_block, w_.page_size, w_.budget, w_.softmax_scale)
+    b = kap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w_.num_kv_heads,
+                               w_.q_block, w_.page_size, w_.budget, w_.softmax_scale,
+                               shared_kv=True)
+    assert w_.num_q_heads == w_.num_kv_heads
+    for f in ("blocks", "pages", "counts", "hrm_counts"):
+        assert np.array_equal(getattr(a, f), getattr(b, f))

@@ -93,6 +93,9 @@ MUTATIONS = [
     # Delta / N: threshold inverted to ln(Delta / N)
     (osk, "tau_from_delta", "math.log(seqlen / delta)", "math.log(delta / seqlen)",
      [to.test_tau_from_delta_hand_values]),
+    # GQA-shared mask: only the first head's proxy rows scored
+    (kap, "group_tiles", "for qb, _, va in pooled]", "for qb, _, va in pooled[:1]]",
+     [tk.test_gqa_shared_golden]),
     # fidelity: exact top-k picks the smallest masses
     (fid, "top_mass_blocks", "-mass))", "mass))",
      [tf.test_top_mass_and_iou_hand_values]),
