@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--logical-skip", action="store_true",
                     help="also time physical page jumping (OSK, skip off) against logical mask "
                          "skipping (cosa_block_mask_prefill) on the same kept sets (extra lines)")
+    ap.add_argument("--shared-kv", action="store_true",
+                    help="also time the KAP + OSK with one mask per KV head shared by its query "
+                         "heads (extra JSON line)")
     ap.add_argument("--only", choices=["all", "kap", "osk", "dense"], default="all",
                     help="launch only one kernel kind (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -248,6 +251,10 @@ def main():
                                   "stage1_budget": round(vis / causal_slots, 5),
                                   "skip_ratio": round(skp / max(vis, 1), 5),
                                   "osk_tflops": round(fl / om / 1e9, 1)}), flush=True)
+    if args.shared_kv:
+        shared_kv_bench(args, w, bk, prob, q, kp, vp, ws, out, stream, ev, causal_slots, fps,
+                        budget, tau, dense_ms)
+
     if args.logical_skip:
         logical_skip_bench(args, w, bk, prob, q, kp, vp, ws, out, stream, ev, causal_slots,
                            dense_ms)
@@ -334,6 +341,38 @@ def remap_ablation(args, w, bk, prob, q, kp, vp, ws, out, stream, ev, causal_slo
                                   round(dense_ms / om, 3),
                                   "osk_tflops": round(fps * (2 * vis - skp) / om / 1e9, 1)}),
                       flush=True)
+
+
+def shared_kv_bench(args, w, bk, prob, q, kp, vp, ws, out, stream, ev, causal_slots, fps,
+                    budget, tau, dense_ms):
+    """KAP + OSK with one mask per KV head shared by its query heads, at the
+    workload's budget and tau (same timing as the main line)."""
+    import torch
+    m2 = bk.proxy_ordered_mask_shared_kv(prob, q, kp, budget, workspace=ws)
+    r2 = bk.osk_prefill_shared_kv(prob, q, kp, vp, m2, tau, record=True)
+    torch.cuda.synchronize()
+    st = r2.row_stats.cpu().numpy().reshape(-1, 2)
+    for _ in range(max(1, args.warmup)):
+        bk.proxy_ordered_mask_shared_kv(prob, q, kp, budget, workspace=ws, out=m2)
+        bk.osk_prefill_shared_kv(prob, q, kp, vp, m2, tau, out=out)
+    e0, e1, e2 = ev(), ev(), ev()
+    e0.record(stream)
+    for _ in range(args.steps):
+        bk.proxy_ordered_mask_shared_kv(prob, q, kp, budget, workspace=ws, out=m2)
+    e1.record(stream)
+    for _ in range(args.steps):
+        bk.osk_prefill_shared_kv(prob, q, kp, vp, m2, tau, out=out)
+    e2.record(stream)
+    torch.cuda.synchronize()
+    km, om = e0.elapsed_time(e1) / args.steps, e1.elapsed_time(e2) / args.steps
+    vis, skp = int(st[:, 0].sum()), int(st[:, 1].sum())
+    print(json.dumps({"shared_kv": w.name, "budget": budget, "tau": tau, "kap_ms": round(km, 4),
+                      "osk_ms": round(om, 4), "ms_per_layer": round(km + om, 4),
+                      "speedup_vs_dense": None if dense_ms is None else
+                      round(dense_ms / (km + om), 3),
+                      "stage1_budget": round(vis / causal_slots, 5),
+                      "skip_ratio": round(skp / max(vis, 1), 5),
+                      "osk_tflops": round(fps * (2 * vis - skp) / om / 1e9, 1)}), flush=True)
 
 
 LOGICAL_SKIP_BUDGETS = (0.5, 0.3, 0.2, 0.1, 0.05)

@@ -6,5 +6,7 @@ does not load the library; the first call does, and raises if the library has
 not been built (``python -m block_sparse_long_kap_amd.build``).
 """
 from .api import (KapWorkspace, OrderedMask, PrefillOutput, Problem,  # noqa: F401
-                  block_mask_prefill, dense_prefill, osk_prefill, osk_prefill_delta, proxy_ordered_mask,
-                  proxy_ordered_mask_top_p, tau_from_delta)
+                  block_mask_prefill, dense_prefill, osk_prefill, osk_prefill_delta,
+                  osk_prefill_shared_kv,
+                  proxy_ordered_mask, proxy_ordered_mask_shared_kv, proxy_ordered_mask_top_p,
+                  tau_from_delta)

@@ -58,6 +58,11 @@ SIGNATURES = {
                                         c_i64, c_vp, c_size, c_vp]),
     "cosa_proxy_ordered_mask_top_p": (c_i32, [P, c_vp, c_vp, c_f32, c_f32, c_vp, c_vp, c_vp,
                                               c_vp, c_vp, c_vp, c_i64, c_vp, c_size, c_vp]),
+    "cosa_proxy_ordered_mask_shared_kv": (c_i32, [P, c_vp, c_vp, c_f32, c_f32, c_vp, c_vp,
+                                                 c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_size,
+                                                 c_vp]),
+    "cosa_osk_prefill_shared_kv": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_f32,
+                                           c_vp, c_vp, c_vp, c_vp, c_vp]),
     "cosa_osk_prefill": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_f32, c_vp, c_vp,
                                  c_vp, c_vp, c_vp]),
     "cosa_osk_prefill_delta": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_f32, c_vp,

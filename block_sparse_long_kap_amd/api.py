@@ -143,12 +143,13 @@ class KapWorkspace:
         self.buf = torch.empty(max(self.nbytes, 1), dtype=torch.uint8, device=problem.device)
 
 
-def _mask_buffers(problem: Problem, q, k_pool, budget, capacity, hrm_counts, debug, out):
+def _mask_buffers(problem: Problem, q, k_pool, budget, capacity, hrm_counts, debug, out,
+                  shared_kv=False):
     problem._check_qkv(q, k_pool)
     dev = problem.device
     C = problem.mask_capacity(budget) if capacity is None else int(capacity)
     nqb = problem.num_q_tiles()
-    rows = (problem.batch, problem.num_q_heads, nqb)
+    rows = (problem.batch, problem.num_kv_heads if shared_kv else problem.num_q_heads, nqb)
     if out is None:
         out = OrderedMask(
             blocks=torch.empty(rows + (C,), dtype=torch.int32, device=dev),
@@ -206,14 +207,16 @@ class PrefillOutput:
     row_stats: Optional[torch.Tensor] = None     # int32 [B][Hq][NQB][2]
 
 
-def _prefill_buffers(problem: Problem, q, k_pool, v_pool, mask, lse, record, out):
+def _prefill_buffers(problem: Problem, q, k_pool, v_pool, mask, lse, record, out,
+                     shared_kv=False):
     problem._check_qkv(q, k_pool, v_pool)
     dev = problem.device
     nqb = problem.num_q_tiles()
     rows = (problem.batch, problem.num_q_heads, nqb)
-    _need(mask.blocks, "mask.blocks", torch.int32, dev, shape=rows + (mask.capacity,))
-    _need(mask.pages, "mask.pages", torch.int32, dev, shape=rows + (mask.capacity,))
-    _need(mask.counts, "mask.counts", torch.int32, dev, shape=rows)
+    mrows = (problem.batch, problem.num_kv_heads, nqb) if shared_kv else rows
+    _need(mask.blocks, "mask.blocks", torch.int32, dev, shape=mrows + (mask.capacity,))
+    _need(mask.pages, "mask.pages", torch.int32, dev, shape=mrows + (mask.capacity,))
+    _need(mask.counts, "mask.counts", torch.int32, dev, shape=mrows)
     if out is None:
         out = PrefillOutput(
             out=torch.empty_like(q),
@@ -237,6 +240,42 @@ def osk_prefill(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor, v_pool:
                               _ptr(out.lse), _ptr(out.skip_record), _ptr(out.row_stats),
                               _stream(problem.device))
     _lib.check(st, "cosa_osk_prefill")
+    return out
+
+
+def proxy_ordered_mask_shared_kv(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor,
+                                 budget: float, top_p: float = 1.0, *,
+                                 capacity: Optional[int] = None, hrm_counts: bool = True,
+                                 debug: bool = False, workspace: Optional[KapWorkspace] = None,
+                                 out: Optional[OrderedMask] = None) -> OrderedMask:
+    """KAP with one mask per KV head shared by its query heads
+    (``cosa_proxy_ordered_mask_shared_kv``); arrays are [B][Hkv][NQB](...)."""
+    lib = _lib.load()
+    out = _mask_buffers(problem, q, k_pool, budget, capacity, hrm_counts, debug, out,
+                        shared_kv=True)
+    ws = workspace if workspace is not None else KapWorkspace(problem)
+    st = lib.cosa_proxy_ordered_mask_shared_kv(
+        problem.ref(), _ptr(q), _ptr(k_pool), ctypes.c_float(top_p), ctypes.c_float(budget),
+        _ptr(out.blocks), _ptr(out.pages), _ptr(out.counts), _ptr(out.hrm_counts),
+        _ptr(out.debug_w), _ptr(out.debug_hrm), out.capacity, _ptr(ws.buf), ws.nbytes,
+        _stream(problem.device))
+    _lib.check(st, "cosa_proxy_ordered_mask_shared_kv")
+    return out
+
+
+def osk_prefill_shared_kv(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor,
+                          v_pool: torch.Tensor, mask: OrderedMask, skip_tau: float, *,
+                          lse: bool = True, record: bool = True,
+                          out: Optional[PrefillOutput] = None) -> PrefillOutput:
+    """Ordered-Skipping Kernel over per-KV-head masks (``cosa_osk_prefill_shared_kv``)."""
+    lib = _lib.load()
+    out = _prefill_buffers(problem, q, k_pool, v_pool, mask, lse, record, out, shared_kv=True)
+    st = lib.cosa_osk_prefill_shared_kv(problem.ref(), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                        _ptr(mask.blocks), _ptr(mask.pages), _ptr(mask.counts),
+                                        mask.capacity, ctypes.c_float(skip_tau), _ptr(out.out),
+                                        _ptr(out.lse), _ptr(out.skip_record),
+                                        _ptr(out.row_stats), _stream(problem.device))
+    _lib.check(st, "cosa_osk_prefill_shared_kv")
     return out
 
 

@@ -192,7 +192,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     return;
   }
   const int tile_last = min(tile_q0 + BQ, L) - 1;
-  const int cnt = kOrdered ? p.counts[row] : tile_last / kPage + 1;
+  // mask row: per query head, or per KV head when the group shares its mask
+  const int64_t mrow =
+      kOrdered ? ((int64_t)b * p.mask_heads + h / (p.hq / p.mask_heads)) * p.nqb + i : row;
+  const int cnt = kOrdered ? p.counts[mrow] : tile_last / kPage + 1;
   if (kLogical) {
     const uint32_t* bits = p.block_mask + row * p.mask_words;
     for (int wd = tid; wd < (cnt + 31) / 32; wd += NT) sBits[wd] = bits[wd];
@@ -206,8 +209,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   };
   // read-only for the whole kernel: lets the uniform slot lookups go
   // through scalar loads instead of vector loads plus a vmcnt wait
-  const int32_t* __restrict__ ob = kOrdered ? p.ordered_blocks + row * p.capacity : nullptr;
-  const int32_t* __restrict__ op = kOrdered ? p.ordered_pages + row * p.capacity : nullptr;
+  const int32_t* __restrict__ ob = kOrdered ? p.ordered_blocks + mrow * p.capacity : nullptr;
+  const int32_t* __restrict__ op = kOrdered ? p.ordered_pages + mrow * p.capacity : nullptr;
   const int32_t* __restrict__ pt = p.page_table + (int64_t)b * p.max_pages;
 
   const int wave_q0 = tile_q0 + wave * 32;

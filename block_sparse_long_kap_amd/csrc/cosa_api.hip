@@ -93,6 +93,7 @@ void fill_attn(cosa::AttnParams& a, const cosa_problem* p, const void* q, const 
   a.counts = nullptr;
   a.skip_record = nullptr;
   a.row_stats = nullptr;
+  a.mask_heads = p->num_q_heads;
   a.block_mask = nullptr;
   a.mask_words = 0;
   a.capacity = 0;
@@ -186,7 +187,7 @@ COSA_EXPORT cosa_status cosa_check_page_table_host(const cosa_problem* p,
 namespace {
 
 cosa_status proxy_mask(const cosa_problem* p, const void* q, const void* k_pool, float budget,
-                       uint64_t top_p_fx, int32_t* ordered_blocks, int32_t* ordered_pages,
+                       uint64_t top_p_fx, bool shared, int32_t* ordered_blocks, int32_t* ordered_pages,
                        int32_t* counts, int32_t* hrm_counts, float* debug_w, uint8_t* debug_hrm,
                        int64_t capacity, void* workspace, size_t workspace_bytes, void* stream) {
   cosa_status st = validate(p);
@@ -226,6 +227,17 @@ cosa_status proxy_mask(const cosa_problem* p, const void* q, const void* k_pool,
   k.beta_ppm = ppm;
   k.scale = p->softmax_scale;
   k.top_p_fx = top_p_fx;
+  k.shared_heads = 0;
+  if (shared) {
+    const int hg = p->num_q_heads / p->num_kv_heads;
+    // one KV head per query head: the shared mask is the per-head mask
+    if (hg > 1) {
+      if (hg * (p->q_block / cosa::kProxyRows) > 32 || (hg & (hg - 1)) != 0)
+        return fail(COSA_ERR_UNSUPPORTED,
+                    "shared masks need (q_heads / kv_heads) * (q_block / 16) <= 32, a power of 2");
+      k.shared_heads = hg;
+    }
+  }
   return hip_status(cosa::launch_kap(k, p->head_dim, p->q_block, (hipStream_t)stream));
 }
 
@@ -238,8 +250,20 @@ COSA_EXPORT cosa_status cosa_proxy_ordered_mask(const cosa_problem* p, const voi
                                                 float* debug_w, uint8_t* debug_hrm,
                                                 int64_t capacity, void* workspace,
                                                 size_t workspace_bytes, void* stream) {
-  return proxy_mask(p, q, k_pool, budget, 0, ordered_blocks, ordered_pages, counts, hrm_counts,
-                    debug_w, debug_hrm, capacity, workspace, workspace_bytes, stream);
+  return proxy_mask(p, q, k_pool, budget, 0, false, ordered_blocks, ordered_pages, counts,
+                    hrm_counts, debug_w, debug_hrm, capacity, workspace, workspace_bytes, stream);
+}
+
+COSA_EXPORT cosa_status cosa_proxy_ordered_mask_shared_kv(
+    const cosa_problem* p, const void* q, const void* k_pool, float top_p, float budget,
+    int32_t* ordered_blocks, int32_t* ordered_pages, int32_t* counts, int32_t* hrm_counts,
+    float* debug_w, uint8_t* debug_hrm, int64_t capacity, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (!(top_p > 0.f) || !(top_p <= 1.f)) return fail(COSA_ERR_INVALID_ARG, "top_p must lie in (0, 1]");
+  const uint64_t fx = top_p >= 1.f ? 0ull : (uint64_t)floor((double)top_p * 281474976710656.0);
+  return proxy_mask(p, q, k_pool, budget, top_p >= 1.f ? 0ull : (fx < 1 ? 1 : fx), true,
+                    ordered_blocks, ordered_pages, counts, hrm_counts, debug_w, debug_hrm,
+                    capacity, workspace, workspace_bytes, stream);
 }
 
 COSA_EXPORT cosa_status cosa_proxy_ordered_mask_top_p(
@@ -250,8 +274,9 @@ COSA_EXPORT cosa_status cosa_proxy_ordered_mask_top_p(
   if (!(top_p > 0.f) || !(top_p <= 1.f)) return fail(COSA_ERR_INVALID_ARG, "top_p must lie in (0, 1]");
   // p * 2^48 rounded down (exact in double); p = 1 keeps every candidate
   const uint64_t fx = top_p >= 1.f ? ~0ull : (uint64_t)floor((double)top_p * 281474976710656.0);
-  return proxy_mask(p, q, k_pool, budget, fx < 1 ? 1 : fx, ordered_blocks, ordered_pages, counts,
-                    hrm_counts, debug_w, debug_hrm, capacity, workspace, workspace_bytes, stream);
+  return proxy_mask(p, q, k_pool, budget, fx < 1 ? 1 : fx, false, ordered_blocks, ordered_pages,
+                    counts, hrm_counts, debug_w, debug_hrm, capacity, workspace, workspace_bytes,
+                    stream);
 }
 
 COSA_EXPORT cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, const void* k_pool,
@@ -274,6 +299,38 @@ COSA_EXPORT cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, c
   a.skip_record = skip_record;
   a.row_stats = row_stats;
   a.capacity = capacity;
+  if (skip_tau >= 0.f) {
+    a.skip_mode = cosa::kSkipTau;
+    a.tau_log2 = skip_tau * 1.4426950408889634f;
+  }
+  return hip_status(
+      cosa::launch_attention(a, p->head_dim, p->q_block, cosa::kModeOrdered, (hipStream_t)stream));
+}
+
+COSA_EXPORT cosa_status cosa_osk_prefill_shared_kv(
+    const cosa_problem* p, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* ordered_blocks, const int32_t* ordered_pages, const int32_t* counts,
+    int64_t capacity, float skip_tau, void* out, float* lse, uint8_t* skip_record,
+    int32_t* row_stats, void* stream) {
+  cosa_status st = validate(p);
+  if (st != COSA_OK) return st;
+  if (q == nullptr || k_pool == nullptr || v_pool == nullptr || out == nullptr ||
+      ordered_blocks == nullptr || ordered_pages == nullptr || counts == nullptr)
+    return fail(COSA_ERR_INVALID_ARG, "q, k_pool, v_pool, out and the mask arrays are required");
+  if (capacity < 1) return fail(COSA_ERR_INVALID_ARG, "capacity must be >= 1");
+  if (isnan(skip_tau)) return fail(COSA_ERR_INVALID_ARG, "skip_tau is NaN");
+  cosa::AttnParams a;
+  fill_attn(a, p, q, k_pool, v_pool, out, lse);
+  a.ordered_blocks = ordered_blocks;
+  a.ordered_pages = ordered_pages;
+  a.counts = counts;
+  a.skip_record = skip_record;
+  a.row_stats = row_stats;
+  a.capacity = capacity;
+  a.mask_heads = p->num_kv_heads;
+  // the heads that share a mask visit the same pages: run them side by side
+  // on one XCD so that those pages are fetched into its L2 once
+  if (a.xcd_units != 0) a.order = cosa::kOrderGroupXcd;
   if (skip_tau >= 0.f) {
     a.skip_mode = cosa::kSkipTau;
     a.tau_log2 = skip_tau * 1.4426950408889634f;

@@ -34,6 +34,7 @@ struct AttnParams {
   const int32_t* counts;          // OSK only
   uint8_t* skip_record;           // OSK only, nullable
   int32_t* row_stats;             // OSK only, nullable
+  int32_t mask_heads;             // OSK: heads of the mask layout (Hq, or Hkv when shared)
   const uint32_t* block_mask;     // logical-skip mode only: [rows][mask_words] bits
   int64_t mask_words;
   int64_t capacity;
@@ -83,6 +84,9 @@ struct KapParams {
   // Top-p mass in fixed point (p * 2^48, rounded down); 0 = budget only,
   // all ones = p of 1 (keep every candidate the budget allows)
   uint64_t top_p_fx;
+  // 0: one mask per query head; else the number of query heads per KV head,
+  // one mask per KV head shared by them
+  int32_t shared_heads;
 };
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, AttnMode mode,

@@ -132,19 +132,25 @@ __device__ __forceinline__ unsigned long long key_mass(uint32_t key_hi) {
   return (unsigned long long)(w * 281474976710656.0f);
 }
 
-template <int D, int R, bool kTopP>
+// HPW = 1: one query head, kTilesPerGroup consecutive tiles per workgroup,
+// one mask row per (sequence, query head, tile).  HPW > 1: the HPW query
+// heads of one KV head, one tile per workgroup, one mask row per (sequence,
+// KV head, tile) shared by those heads (their proxy rows scored together).
+template <int D, int R, bool kTopP, int HPW>
 __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   constexpr int NT = 256;
   constexpr int NWAVE = NT / 64;
-  constexpr int TPW = kTilesPerGroup;
-  constexpr int MR = TPW * R;                 // proxy rows of the group (16 or 32)
+  constexpr bool kShared = HPW > 1;
+  constexpr int TPW = kShared ? 1 : kTilesPerGroup;
+  constexpr int RPT = HPW * R;                // proxy rows per tile
+  constexpr int MR = TPW * RPT;               // proxy rows of the workgroup (<= 32)
   constexpr int BQ = R * kProxyRows;
   constexpr int KSTEPS = D / 16;
   constexpr int KCH = D / 8;
   static_assert(MR <= 32, "one 32-row MFMA operand");
 
-  // 64 KB of sort keys; the pooled queries (2 x 32 x D bf16) live in the
-  // same space before the keys are built
+  // 16 KB of sort keys per tile; the pooled queries (2 x 32 x D bf16) live in
+  // the same space before the keys are built
   __shared__ __attribute__((aligned(16))) unsigned long long sKey[TPW][kMaxCandidates];
   __shared__ RowStat sStat[NWAVE][32];
   __shared__ float sRowM[32];
@@ -170,14 +176,17 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   // GQA group side by side.
   const int ngroups = (p.nqb + TPW - 1) / TPW;
   const int hg = p.hq / p.hkv;
-  const int per_kv = ngroups * hg;
+  const int per_kv = kShared ? ngroups : ngroups * hg;
   const int G = blockIdx.x / per_kv;
   const int rem = blockIdx.x - G * per_kv;
-  const int level = rem / hg;
+  const int level = kShared ? rem : rem / hg;
   const int b = G / p.hkv;
   const int g = G - b * p.hkv;
-  const int h = g * hg + (rem - level * hg);
+  const int h = kShared ? g * hg : g * hg + (rem - level * hg);   // first (or only) head
   const int i0 = (ngroups - 1 - level) * TPW;
+  // mask rows: (b, query head) or (b, KV head)
+  const int64_t mrow0 = kShared ? ((int64_t)b * p.hkv + g) * p.nqb
+                                : ((int64_t)b * p.hq + h) * p.nqb;
   const int q0 = p.cu_seqlens[b];
   const int L = p.cu_seqlens[b + 1] - q0;
   const int nkb = (L + kPage - 1) / kPage;
@@ -191,15 +200,17 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     const int i = i0 + t;
     const bool valid = i < p.nqb && i * BQ < L;
     n_t[t] = valid ? (min((i + 1) * BQ, L) - 1) / kPage + 1 : 0;
-    rows_t[t] = valid ? min(R, (L - i * BQ + kProxyRows - 1) / kProxyRows) : 0;
+    rows_t[t] = valid ? HPW * min(R, (L - i * BQ + kProxyRows - 1) / kProxyRows) : 0;
     n_wg = max(n_wg, n_t[t]);
   }
   // rows that are past the end of the sequence (or of the group) have no
   // candidates; cand(m) = number of candidate blocks of proxy row m
+  // proxy row m: tile m / RPT, head (m / R) % HPW, row m % R of that tile
   auto row_cand = [&](int m) -> int {
     if (m >= MR) return 0;
-    const int start = (i0 + m / R) * BQ + (m % R) * kProxyRows;
-    if (i0 + m / R >= p.nqb || start >= L) return 0;
+    const int i = i0 + m / RPT;
+    const int start = i * BQ + (m % R) * kProxyRows;
+    if (i >= p.nqb || start >= L) return 0;
     return (min(start + kProxyRows, L) - 1) / kPage + 1;
   };
 
@@ -207,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     for (int t = 0; t < TPW; ++t) {
       const int i = i0 + t;
       if (i >= p.nqb) break;
-      const int64_t row = ((int64_t)b * p.hq + h) * p.nqb + i;
+      const int64_t row = mrow0 + i;
       for (int s = tid; s < p.capacity; s += NT) {
         p.ordered_blocks[row * p.capacity + s] = -1;
         p.ordered_pages[row * p.capacity + s] = -1;
@@ -239,11 +250,12 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
       const int m = idx / KCH, c = idx % KCH;
       nrow[e] = 0;
       int start = 0;
-      if (m < MR && i0 + m / R < p.nqb) {
-        start = (i0 + m / R) * BQ + (m % R) * kProxyRows;
+      if (m < MR && i0 + m / RPT < p.nqb) {
+        start = (i0 + m / RPT) * BQ + (m % R) * kProxyRows;
         nrow[e] = max(min(start + kProxyRows, L) - start, 0);
       }
-      const uint16_t* src = p.q + ((int64_t)(q0 + start) * p.hq + h) * D + c * 8;
+      const int hq_m = h + (m / R) % HPW;   // the row's query head
+      const uint16_t* src = p.q + ((int64_t)(q0 + start) * p.hq + hq_m) * D + c * 8;
 #pragma unroll
       for (int t = 0; t < kProxyRows; ++t) {
         v[e][t] = (u32x4_t){0u, 0u, 0u, 0u};
@@ -377,12 +389,12 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
       const float w = wsum / (float)rows_t[t];
       bool hrm = false;
 #pragma unroll
-      for (int r = 0; r < R; ++r) hrm |= (sRowA[t * R + r] == j);
+      for (int r = 0; r < RPT; ++r) hrm |= (sRowA[t * RPT + r] == j);
       if (hrm) atomicAdd(&sHrm[t], 1);
       const uint32_t wb = __float_as_uint(w);   // w >= 0: bit order == value order
       key = ((unsigned long long)(hrm ? 0u : 1u) << 63) |
             ((unsigned long long)(0x7FFFFFFFu - wb) << 32) | (uint32_t)j;
-      const int64_t row = ((int64_t)b * p.hq + h) * p.nqb + i;
+      const int64_t row = mrow0 + i;
       if (p.debug_w != nullptr) p.debug_w[row * p.n_max + j] = w;
       if (p.debug_hrm != nullptr) p.debug_hrm[row * p.n_max + j] = hrm ? 1 : 0;
     }
@@ -403,7 +415,12 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
       }
       part[g4] = sum;
     }
-    if (R == 8) {
+    if (kShared) {
+      // one tile: every row of the accumulator
+      const float w = part[0] + part[1] + part[2] + part[3];
+      const float wt = w + __shfl_xor(w, 32);
+      if (hf == 0) emit(0, j, wt);
+    } else if (R == 8) {
       // tile g4 = rows 8g4 .. 8g4+7: four in this lane, four in lane ^ 32
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -427,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   // the k-th smallest key on its upper 32 bits (HRM flag and -w), keep every
   // key below that value and every key equal to it (ties are broken by the
   // block index in the sort that follows), compacted in place.
-  static_assert(TPW == NWAVE, "one wave per tile of the group");
+  static_assert(TPW <= NWAVE, "one wave per tile of the group");
   int k_t[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
@@ -439,7 +456,7 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     }
     k_t[t] = k;
   }
-  {
+  if (wave < TPW) {
     const int t = wave;
     const int n = n_t[t];
     int k = k_t[t];
@@ -619,7 +636,7 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   for (int t = 0; t < TPW; ++t) {
     const int i = i0 + t;
     if (i >= p.nqb) break;
-    const int64_t row = ((int64_t)b * p.hq + h) * p.nqb + i;
+    const int64_t row = mrow0 + i;
     const int n = n_t[t];
     const int k = k_t[t];
     for (int s = tid; s < p.capacity; s += NT) {
@@ -650,12 +667,32 @@ hipError_t launch_kap_t(const KapParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((kap_pool_keys<D>), dim3(nkb, p.batch), dim3(256), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (p.shared_heads > 1) {
+    const int64_t grid = (int64_t)p.batch * p.hkv * p.nqb;
+#define COSA_KAP_SHARED(HPW_)                                                                \
+  if constexpr (HPW_ * R <= 32) {                                                          \
+    if (p.shared_heads == HPW_) {                                                          \
+      if (top_p)                                                                           \
+        hipLaunchKernelGGL((kap_select<D, R, true, HPW_>), dim3((unsigned)grid), dim3(256),  \
+                           0, stream, p);                                                  \
+      else                                                                                 \
+        hipLaunchKernelGGL((kap_select<D, R, false, HPW_>), dim3((unsigned)grid), dim3(256), \
+                           0, stream, p);                                                  \
+      return hipGetLastError();                                                            \
+    }                                                                                      \
+  }
+    COSA_KAP_SHARED(2)
+    COSA_KAP_SHARED(4)
+    COSA_KAP_SHARED(8)
+#undef COSA_KAP_SHARED
+    return hipErrorInvalidValue;
+  }
   const int64_t groups = (p.nqb + kTilesPerGroup - 1) / kTilesPerGroup;
   const int64_t grid = (int64_t)p.batch * p.hq * groups;
   if (top_p)
-    hipLaunchKernelGGL((kap_select<D, R, true>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((kap_select<D, R, true, 1>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((kap_select<D, R, false>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((kap_select<D, R, false, 1>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

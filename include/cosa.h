@@ -174,6 +174,32 @@ cosa_status cosa_proxy_ordered_mask_top_p(const cosa_problem* p, const void* q,
                                           size_t workspace_bytes, void* stream);
 
 /*
+ * Kernel-Aware Proxy with one mask per KV head, shared by the query heads that
+ * read it (grouped-query attention; the pages leave the packing of a KV
+ * group to the implementation, pp §4.3 / App. D.1 name only the per-tile
+ * mask).  For mask row (b, g, i) the proxy rows of tile i of every query
+ * head h with h / (num_q_heads / num_kv_heads) == g are scored together
+ * against the pooled keys of KV head g: w_j is the mean over all of them of
+ * their per-row softmax, HRM_j marks the arg-max block of any of them; order,
+ * budget and remap as for cosa_proxy_ordered_mask().  top_p in (0, 1] as for
+ * cosa_proxy_ordered_mask_top_p() (1 = budget only).
+ *
+ * Mask arrays are laid out per KV head: ordered_blocks / ordered_pages
+ * [batch][num_kv_heads][NQB][capacity], counts / hrm_counts
+ * [batch][num_kv_heads][NQB], debug_w / debug_hrm [..][NQB][n_max].
+ * Requires (num_q_heads / num_kv_heads) a power of two with
+ * (num_q_heads / num_kv_heads) * q_block / 16 <= 32 (COSA_ERR_UNSUPPORTED
+ * otherwise); with one query head per KV head it equals the per-head mask.
+ */
+cosa_status cosa_proxy_ordered_mask_shared_kv(const cosa_problem* p, const void* q,
+                                              const void* k_pool, float top_p, float budget,
+                                              int32_t* ordered_blocks, int32_t* ordered_pages,
+                                              int32_t* counts, int32_t* hrm_counts,
+                                              float* debug_w, uint8_t* debug_hrm,
+                                              int64_t capacity, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+
+/*
  * Ordered-Skipping Kernel (CoSA (paperpeel) §4.3, App. D.1; skip rule §3.3).
  *
  * For every mask row (b, h, i) the kernel walks slots t = 0..counts[row]-1 in
@@ -202,6 +228,21 @@ cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, const void* k
                              const int32_t* ordered_pages, const int32_t* counts,
                              int64_t capacity, float skip_tau, void* out, float* lse,
                              uint8_t* skip_record, int32_t* row_stats, void* stream);
+
+/*
+ * Ordered-Skipping Kernel over masks shared per KV head (the layout of
+ * cosa_proxy_ordered_mask_shared_kv()): query head h of sequence b, tile i
+ * walks mask row (b, h / (num_q_heads / num_kv_heads), i).  Everything else,
+ * including the per-head, per-tile skip vote and the per-head skip_record /
+ * row_stats layout [batch][num_q_heads][NQB](...), is as for
+ * cosa_osk_prefill().  The query heads of one KV head run side by side on one
+ * XCD so that the pages they share are fetched into its L2 once.
+ */
+cosa_status cosa_osk_prefill_shared_kv(const cosa_problem* p, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* ordered_blocks,
+                                       const int32_t* ordered_pages, const int32_t* counts,
+                                       int64_t capacity, float skip_tau, void* out, float* lse,
+                                       uint8_t* skip_record, int32_t* row_stats, void* stream);
 
 /*
  * Ordered-Skipping Kernel with the length-adaptive threshold Delta / N

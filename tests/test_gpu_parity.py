@@ -79,9 +79,11 @@ def test_dense_matches_oracle(case):
     ls.assert_ok(max_abs=1e-3, mean_abs=1e-4, label=f"dense {name} lse")
 
 
-def _run_osk_vs_oracle(w, x, blocks, counts, tau, label, tiles=None, delta=None):
+def _run_osk_vs_oracle(w, x, blocks, counts, tau, label, tiles=None, delta=None,
+                       shared=False):
     """OSK through the C ABI against the closed-form oracle tile by tile; with
-    ``delta`` the length-adaptive entry point and tau_b = ln(L_b / delta)."""
+    ``delta`` the length-adaptive entry point and tau_b = ln(L_b / delta); with
+    ``shared`` the masks are per KV head (cosa_osk_prefill_shared_kv)."""
     prob, q, k, v = upload(x, DEV)
     C = blocks.shape[-1]
     pages = np.where(blocks >= 0, 0, -1).astype(np.int32)
@@ -91,7 +93,12 @@ def _run_osk_vs_oracle(w, x, blocks, counts, tau, label, tiles=None, delta=None)
     mask = bk.OrderedMask(blocks=torch.from_numpy(blocks).to(DEV),
                           pages=torch.from_numpy(pages).to(DEV),
                           counts=torch.from_numpy(counts).to(DEV), hrm_counts=None, capacity=C)
-    if delta is None:
+    if shared:
+        res = bk.osk_prefill_shared_kv(prob, q, k, v, mask, tau)
+        # the oracle walks each query head's copy of its KV head's row
+        grp_ = w.num_q_heads // w.num_kv_heads
+        blocks, counts = np.repeat(blocks, grp_, axis=1), np.repeat(counts, grp_, axis=1)
+    elif delta is None:
         res = bk.osk_prefill(prob, q, k, v, mask, tau)
     else:
         res = bk.osk_prefill_delta(prob, q, k, v, mask, delta)
@@ -399,3 +406,61 @@ def test_block_mask_logical_skip_matches_oracle(case):
     # the same set through the OSK (skip off) agrees with it to rounding order
     d = np.abs(_np(osk.out).astype(np.float64) - out)
     assert d.max() <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# KV-group-shared masks (cosa_proxy_ordered_mask_shared_kv, cosa_osk_prefill_shared_kv)
+
+
+@pytest.mark.parametrize("case", [("tiny", dict(RAGGED), 0.3, 1.0),
+                                  ("tiny", dict(RAGGED, q_block=64), 0.2, 1.0),
+                                  ("tiny", dict(RAGGED, num_q_heads=4), 0.5, 1.0),
+                                  ("tiny", dict(RAGGED), 1.0, 0.9),
+                                  ("tiny_skip", {}, 0.5, 1.0)])
+def test_kap_shared_kv_matches_oracle(case):
+    name, kw, budget, top_p = case
+    w, x = _inputs(name, **kw)
+    print(f"[case] kap shared {name} {kw} budget={budget} top_p={top_p}", flush=True)
+    prob, q, k, v = upload(x, DEV)
+    gm = bk.proxy_ordered_mask_shared_kv(prob, q, k, budget, top_p, debug=True)
+    torch.cuda.synchronize()
+    gb, gp, gc, gh = _np(gm.blocks), _np(gm.pages), _np(gm.counts), _np(gm.hrm_counts)
+    dw, dh = _np(gm.debug_w), _np(gm.debug_hrm)
+    beta = okap.budget_ppm(budget)
+    grp = w.num_q_heads // w.num_kv_heads
+    assert gb.shape[1] == w.num_kv_heads
+    exact = ties = 0
+    tp = None if top_p >= 1.0 else top_p
+    for b in range(w.batch):
+        s0, L = int(x.cu_seqlens[b]), int(x.seqlens[b])
+        nqb = (L + w.q_block - 1) // w.q_block
+        assert np.all(gc[b, :, nqb:] == 0)
+        if L == 0:
+            continue
+        kk = materialise(x.k_pool, x.page_table[b], L, w.page_size)
+        for g in range(w.num_kv_heads):
+            qs = [x.q[s0:s0 + L, h].astype(np.float64) for h in range(g * grp, (g + 1) * grp)]
+            res = okap.group_tiles(qs, kk[:, g], w.softmax_scale, w.q_block, w.page_size, beta,
+                                   top_p=tp)
+            for i, tile in res.items():
+                c = int(gc[b, g, i])
+                want = _fixed_point_selection(dw[b, g, i], dh[b, g, i], tile.n, beta,
+                                              1.0 if tp is None else tp)
+                assert c == len(want) and np.array_equal(gb[b, g, i, :c], want), (b, g, i)
+                if tp is not None:
+                    assert c in _allowed_counts(tile, tp, beta), (b, g, i, c, tile.k)
+                kind = check_kap_row(gb[b, g, i], gp[b, g, i], c, gh[b, g, i],
+                                     dataclasses.replace(tile, k=c), x.page_table[b])
+                exact += kind == "exact" and c == tile.k
+                ties += kind == "tie" or c != tile.k
+    print(f"[parity] kap shared {name}: rows exact={exact} near-tie={ties}")
+    assert exact > 0 and ties <= max(1, exact // 100)
+
+
+@pytest.mark.parametrize("tau", [-1.0, 4.0])
+def test_osk_shared_kv_masks(tau):
+    w, x = _inputs("tiny", **dict(RAGGED, q_dir_gain=6.0))
+    print(f"[case] osk shared masks tau={tau}", flush=True)
+    m = okap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
+                                w.q_block, w.page_size, 0.3, w.softmax_scale, shared_kv=True)
+    _run_osk_vs_oracle(w, x, m.blocks, m.counts, tau, f"osk shared tau={tau}", shared=True)
