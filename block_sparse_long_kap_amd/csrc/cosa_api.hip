@@ -224,6 +224,8 @@ cosa_status proxy_mask(const cosa_problem* p, const void* q, const void* k_pool,
   k.max_pages = p->max_pages_per_seq;
   k.nqb = (int32_t)ceil_div(p->max_seqlen, p->q_block);
   k.n_max = (int32_t)n_max;
+  k.kv_block = p->kv_block;
+  k.ppb = p->kv_block / p->page_size;
   k.beta_ppm = ppm;
   k.scale = p->softmax_scale;
   k.top_p_fx = top_p_fx;

@@ -79,6 +79,8 @@ struct KapParams {
   uint8_t* debug_hrm;             // nullable [rows][n_max]
   int64_t capacity;
   int32_t batch, hq, hkv, max_pages, nqb, n_max;
+  int32_t kv_block;               // tokens per logical key block (1 or 2 pages)
+  int32_t ppb;                    // pages per logical block
   int32_t beta_ppm;
   float scale;
   // Top-p mass in fixed point (p * 2^48, rounded down); 0 = budget only,

@@ -65,13 +65,13 @@ __global__ __launch_bounds__(256) void kap_pool_keys(const KapParams p) {
   constexpr int RG = NT / KCH;        // row groups
   __shared__ float red[RG][D];
 
-  const int j = blockIdx.x;
+  const int j = blockIdx.x;   // logical key block (p.ppb pages of kPage keys)
   const int b = blockIdx.y;
   const int q0 = p.cu_seqlens[b];
   const int L = p.cu_seqlens[b + 1] - q0;
-  if (j * kPage >= L) return;
-  const int nvalid = min(kPage, L - j * kPage);
-  const int page = p.page_table[(int64_t)b * p.max_pages + j];
+  if (j * p.kv_block >= L) return;
+  const int nvalid = min(p.kv_block, L - j * p.kv_block);
+  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages + (int64_t)j * p.ppb;
   const int tid = threadIdx.x;
   const int c = tid % KCH;
   const int rg = tid / KCH;
@@ -79,12 +79,13 @@ __global__ __launch_bounds__(256) void kap_pool_keys(const KapParams p) {
   const int64_t plane = (int64_t)p.batch * p.hkv * p.n_max * D;
 
   for (int g = 0; g < p.hkv; ++g) {
-    const uint16_t* base = p.k_pool + ((int64_t)page * p.hkv + g) * (kPage * D) + c * 8;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     for (int r = rg; r < nvalid; r += RG) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(base + r * D);
+      const int page = pt[r / kPage];
+      const uint16_t* base = p.k_pool + ((int64_t)page * p.hkv + g) * (kPage * D) + c * 8;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(base + (r % kPage) * D);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         acc[2 * w] += bf16_lo(v[w]);
@@ -189,7 +190,8 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
                                 : ((int64_t)b * p.hq + h) * p.nqb;
   const int q0 = p.cu_seqlens[b];
   const int L = p.cu_seqlens[b + 1] - q0;
-  const int nkb = (L + kPage - 1) / kPage;
+  const int kvb = p.kv_block;
+  const int nkb = (L + kvb - 1) / kvb;
   const int32_t* __restrict__ pt = p.page_table + (int64_t)b * p.max_pages;
 
   // per-tile sizes (n = 0 for a tile past the sequence's end)
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   for (int t = 0; t < TPW; ++t) {
     const int i = i0 + t;
     const bool valid = i < p.nqb && i * BQ < L;
-    n_t[t] = valid ? (min((i + 1) * BQ, L) - 1) / kPage + 1 : 0;
+    n_t[t] = valid ? (min((i + 1) * BQ, L) - 1) / kvb + 1 : 0;
     rows_t[t] = valid ? HPW * min(R, (L - i * BQ + kProxyRows - 1) / kProxyRows) : 0;
     n_wg = max(n_wg, n_t[t]);
   }
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     const int i = i0 + m / RPT;
     const int start = i * BQ + (m % R) * kProxyRows;
     if (i >= p.nqb || start >= L) return 0;
-    return (min(start + kProxyRows, L) - 1) / kPage + 1;
+    return (min(start + kProxyRows, L) - 1) / kvb + 1;
   };
 
   if (n_wg == 0) {
@@ -219,10 +221,9 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
       const int i = i0 + t;
       if (i >= p.nqb) break;
       const int64_t row = mrow0 + i;
-      for (int s = tid; s < p.capacity; s += NT) {
-        p.ordered_blocks[row * p.capacity + s] = -1;
-        p.ordered_pages[row * p.capacity + s] = -1;
-      }
+      for (int s = tid; s < p.capacity; s += NT) p.ordered_blocks[row * p.capacity + s] = -1;
+      for (int s = tid; s < p.capacity * p.ppb; s += NT)
+        p.ordered_pages[row * p.capacity * p.ppb + s] = -1;
       if (tid == 0) {
         p.counts[row] = 0;
         if (p.hrm_counts != nullptr) p.hrm_counts[row] = 0;
@@ -640,13 +641,15 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     const int n = n_t[t];
     const int k = k_t[t];
     for (int s = tid; s < p.capacity; s += NT) {
-      int blk = -1, pg = -1;
-      if (s < k) {
-        blk = (int)(sKey[t][s] & 0xFFFFFFFFu);
-        pg = pt[blk];
-      }
+      int blk = -1;
+      if (s < k) blk = (int)(sKey[t][s] & 0xFFFFFFFFu);
       p.ordered_blocks[row * p.capacity + s] = blk;
-      p.ordered_pages[row * p.capacity + s] = pg;
+      // the block's pages; -1 for a page past the sequence's end
+      for (int e = 0; e < p.ppb; ++e) {
+        int pg = -1;
+        if (blk >= 0 && blk * kvb + e * kPage < L) pg = pt[blk * p.ppb + e];
+        p.ordered_pages[(row * p.capacity + s) * p.ppb + e] = pg;
+      }
     }
     if (tid == 0) {
       p.counts[row] = k;
