@@ -58,17 +58,20 @@ class Problem:
     q_block: int = 128
     page_size: int = 64
     softmax_scale: Optional[float] = None
+    kv_block: Optional[int] = None   # logical key block; default one page
 
     def __post_init__(self):
         if self.softmax_scale is None:
             self.softmax_scale = 1.0 / math.sqrt(self.head_dim)
+        if self.kv_block is None:
+            self.kv_block = self.page_size
         dev = self.cu_seqlens.device
         _need(self.cu_seqlens, "cu_seqlens", torch.int32, dev, ndim=1)
         _need(self.page_table, "page_table", torch.int32, dev, ndim=2)
         self._c = _lib.CosaProblem(
             batch=self.cu_seqlens.numel() - 1, num_q_heads=self.num_q_heads,
             num_kv_heads=self.num_kv_heads, head_dim=self.head_dim, q_block=self.q_block,
-            kv_block=self.page_size, page_size=self.page_size, max_seqlen=self.max_seqlen,
+            kv_block=self.kv_block, page_size=self.page_size, max_seqlen=self.max_seqlen,
             max_pages_per_seq=self.page_table.shape[1], num_pages=self.num_pages,
             total_q=self.total_q, softmax_scale=self.softmax_scale,
             cu_seqlens=self.cu_seqlens.data_ptr(), page_table=self.page_table.data_ptr())
@@ -151,14 +154,15 @@ def _mask_buffers(problem: Problem, q, k_pool, budget, capacity, hrm_counts, deb
     nqb = problem.num_q_tiles()
     rows = (problem.batch, problem.num_kv_heads if shared_kv else problem.num_q_heads, nqb)
     if out is None:
+        ppb = problem.kv_block // problem.page_size
         out = OrderedMask(
             blocks=torch.empty(rows + (C,), dtype=torch.int32, device=dev),
-            pages=torch.empty(rows + (C,), dtype=torch.int32, device=dev),
+            pages=torch.empty(rows + (C * ppb,), dtype=torch.int32, device=dev),
             counts=torch.empty(rows, dtype=torch.int32, device=dev),
             hrm_counts=torch.empty(rows, dtype=torch.int32, device=dev) if hrm_counts else None,
             capacity=C)
         if debug:
-            n_max = -(-problem.max_seqlen // problem.page_size)
+            n_max = -(-problem.max_seqlen // problem.kv_block)
             out.debug_w = torch.empty(rows + (n_max,), dtype=torch.float32, device=dev)
             out.debug_hrm = torch.empty(rows + (n_max,), dtype=torch.uint8, device=dev)
     return out
@@ -215,7 +219,8 @@ def _prefill_buffers(problem: Problem, q, k_pool, v_pool, mask, lse, record, out
     rows = (problem.batch, problem.num_q_heads, nqb)
     mrows = (problem.batch, problem.num_kv_heads, nqb) if shared_kv else rows
     _need(mask.blocks, "mask.blocks", torch.int32, dev, shape=mrows + (mask.capacity,))
-    _need(mask.pages, "mask.pages", torch.int32, dev, shape=mrows + (mask.capacity,))
+    ppb = problem.kv_block // problem.page_size
+    _need(mask.pages, "mask.pages", torch.int32, dev, shape=mrows + (mask.capacity * ppb,))
     _need(mask.counts, "mask.counts", torch.int32, dev, shape=mrows)
     if out is None:
         out = PrefillOutput(

@@ -139,10 +139,15 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, int bid, int& b
   }
 }
 
-template <int D, int NW, int kMode>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p) {
+// PPB = pages per logical key block (1: a 64-key block is one page; 2: a
+// 128-key block is resolved through two pages, with one vote per block).
+template <int D, int NW, int kMode, int PPB>
+__global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(const AttnParams p) {
   constexpr bool kOrdered = kMode == kModeOrdered;
   constexpr bool kLogical = kMode == kModeLogical;
+  static_assert(PPB == 1 || PPB == 2, "one or two pages per logical block");
+  constexpr int KVB = kPage * PPB;                   // keys per logical block
+  constexpr int MB = 2 * PPB;                        // 32-key S^T blocks per logical block
   constexpr int NT = NW * 64;
   constexpr int BQ = NW * 32;
   constexpr int KCH = D / 8;                         // 16-byte chunks per key row
@@ -159,16 +164,29 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   // Two buffers per operand as distinct LDS objects, so that the compiler
   // can tell reads of one buffer from the asynchronous HBM->LDS copies into
   // the other and does not wait for those copies before the reads.
+  // Buffer (b, s) holds page s of the logical block in flight in slot b.
+  constexpr int kXtra = PPB == 2 ? PageLayout<D>::kBytes : 16;
   __shared__ __attribute__((aligned(16))) unsigned char sK0[PageLayout<D>::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char sK1[PageLayout<D>::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sK2[kXtra];
+  __shared__ __attribute__((aligned(16))) unsigned char sK3[kXtra];
   __shared__ __attribute__((aligned(16))) unsigned char sV0[PageLayout<D>::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char sV1[PageLayout<D>::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sV2[kXtra];
+  __shared__ __attribute__((aligned(16))) unsigned char sV3[kXtra];
   __shared__ int sVote[2][NW];
-  __shared__ int sSlot[2][2][64];   // [page | block][ring chunk][slot]
+  __shared__ int sSlotP[2][64 * PPB];   // [ring chunk][slot * PPB + page]
+  __shared__ int sSlotB[2][64];         // [ring chunk][slot]: logical block
   // logical-skip mode: the tile's block bitmask (up to 16384 causal blocks)
   __shared__ uint32_t sBits[kLogical ? 512 : 1];
-  auto kbuf = [&](int buf) -> unsigned char* { return buf ? sK1 : sK0; };
-  auto vbuf_of = [&](int buf) -> unsigned char* { return buf ? sV1 : sV0; };
+  auto kbuf = [&](int buf, int s) -> unsigned char* {
+    const int x = buf * PPB + s;
+    return x == 0 ? sK0 : x == 1 ? sK1 : x == 2 ? sK2 : sK3;
+  };
+  auto vbuf_of = [&](int buf, int s) -> unsigned char* {
+    const int x = buf * PPB + s;
+    return x == 0 ? sV0 : x == 1 ? sV1 : x == 2 ? sV2 : sV3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -195,7 +213,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   // mask row: per query head, or per KV head when the group shares its mask
   const int64_t mrow =
       kOrdered ? ((int64_t)b * p.mask_heads + h / (p.hq / p.mask_heads)) * p.nqb + i : row;
-  const int cnt = kOrdered ? p.counts[mrow] : tile_last / kPage + 1;
+  const int cnt = kOrdered ? p.counts[mrow] : tile_last / KVB + 1;
   if (kLogical) {
     const uint32_t* bits = p.block_mask + row * p.mask_words;
     for (int wd = tid; wd < (cnt + 31) / 32; wd += NT) sBits[wd] = bits[wd];
@@ -210,7 +228,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   // read-only for the whole kernel: lets the uniform slot lookups go
   // through scalar loads instead of vector loads plus a vmcnt wait
   const int32_t* __restrict__ ob = kOrdered ? p.ordered_blocks + mrow * p.capacity : nullptr;
-  const int32_t* __restrict__ op = kOrdered ? p.ordered_pages + mrow * p.capacity : nullptr;
+  const int32_t* __restrict__ op =
+      kOrdered ? p.ordered_pages + mrow * p.capacity * PPB : nullptr;
   const int32_t* __restrict__ pt = p.page_table + (int64_t)b * p.max_pages;
 
   const int wave_q0 = tile_q0 + wave * 32;
@@ -236,36 +255,47 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   // loop).  When slot 64c starts, wave 0 copies chunk c+1 from memory straight
   // into the ring half that chunk c-1 used (HBM -> LDS); it is read 62 slots
   // and as many barriers later.
+  // page entries: slot t's pages at page_src[t * PPB + s] (the ordered
+  // mask's page list, or the page table, whose logical block t spans pages
+  // t * PPB .. t * PPB + PPB - 1)
   const int32_t* __restrict__ page_src = kOrdered ? op : pt;
-  auto chunk_entry = [&](const int32_t* src, int c) -> int {
-    const int t = c * 64 + lane;
-    return t < cnt ? src[t] : 0;
-  };
   if (wave == 0) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      sSlot[0][c][lane] = chunk_entry(page_src, c);
-      if (kOrdered) sSlot[1][c][lane] = chunk_entry(ob, c);
+#pragma unroll
+      for (int e = 0; e < PPB; ++e) {
+        const int x = c * 64 * PPB + e * 64 + lane;
+        sSlotP[c][e * 64 + lane] = x < cnt * PPB ? page_src[x] : 0;
+      }
+      if (kOrdered) {
+        const int t = c * 64 + lane;
+        sSlotB[c][lane] = t < cnt ? ob[t] : 0;
+      }
     }
   }
   __syncthreads();   // every wave reads the ring (and bitmask) just filled
-  auto slot_page = [&](int t) -> int {
-    return __builtin_amdgcn_readfirstlane(sSlot[0][(t >> 6) & 1][t & 63]);
+  auto slot_page = [&](int t, int s) -> int {
+    return __builtin_amdgcn_readfirstlane(sSlotP[(t >> 6) & 1][(t & 63) * PPB + s]);
   };
   auto slot_block = [&](int t) -> int {
-    return kOrdered ? __builtin_amdgcn_readfirstlane(sSlot[1][(t >> 6) & 1][t & 63]) : t;
+    return kOrdered ? __builtin_amdgcn_readfirstlane(sSlotB[(t >> 6) & 1][t & 63]) : t;
   };
   auto advance_chunks = [&](int t_next) {
     if (wave == 0 && (t_next & 63) == 0 && t_next > 0 && ((t_next >> 6) + 1) * 64 < cnt) {
       const int c = (t_next >> 6) + 1;
-      const int t = min(c * 64 + lane, cnt - 1);   // lanes past the count re-read a valid entry
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(page_src + t),
-                                       (__attribute__((address_space(3))) void*)&sSlot[0][c & 1][0],
-                                       4, 0, 0);
+#pragma unroll
+      for (int e = 0; e < PPB; ++e) {
+        // lanes past the count re-read a valid entry
+        const int x = min(c * 64 * PPB + e * 64 + lane, cnt * PPB - 1);
+        __builtin_amdgcn_global_load_lds(
+            static_cast<const void*>(page_src + x),
+            (__attribute__((address_space(3))) void*)&sSlotP[c & 1][e * 64], 4, 0, 0);
+      }
+      const int t = min(c * 64 + lane, cnt - 1);
       if (kOrdered)
         __builtin_amdgcn_global_load_lds(
             static_cast<const void*>(ob + t),
-            (__attribute__((address_space(3))) void*)&sSlot[1][c & 1][0], 4, 0, 0);
+            (__attribute__((address_space(3))) void*)&sSlotB[c & 1][0], 4, 0, 0);
       // once per 64 slots: keeps any ring copy from being outstanding across
       // the loop back-edge, where the compiler would wait for it (and for the
       // page prefetches) before every QK
@@ -289,8 +319,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
           (__attribute__((address_space(3))) void*)(dst + (e * NT + wave * 64) * 16), 16, 0, 0);
     }
   };
-  auto copy_k = [&](int page, int buf) { copy_page(p.k_pool, page, kbuf(buf)); };
-  auto copy_v = [&](int page, int buf) { copy_page(p.v_pool, page, vbuf_of(buf)); };
+  // the pages of slot t's logical block j that hold keys of the sequence
+  auto copy_k = [&](int t, int j, int buf) {
+#pragma unroll
+    for (int s = 0; s < PPB; ++s)
+      if (s == 0 || j * KVB + s * kPage < L) copy_page(p.k_pool, slot_page(t, s), kbuf(buf, s));
+  };
+  auto copy_v = [&](int t, int j, int buf) {
+#pragma unroll
+    for (int s = 0; s < PPB; ++s)
+      if (s == 0 || j * KVB + s * kPage < L) copy_page(p.v_pool, slot_page(t, s), vbuf_of(buf, s));
+  };
 
   f32x16_t o[DBLK];
 #pragma unroll
@@ -306,14 +345,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
 
   // ---- building blocks of one page step (all straight-line code, so that
   // the compiler can interleave them inside one basic block)
-  // S^T(page) = K Q^T for this wave's 32 queries: raw dot products
-  auto qk = [&](const unsigned char* kb, f32x16_t (&sacc)[2]) {
+  // S^T(block) = K Q^T for this wave's 32 queries: raw dot products; S^T
+  // block mb holds keys 32mb.. of the logical block (page mb / 2)
+  auto qk = [&](int buf, f32x16_t (&sacc)[MB]) {
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-            kb + PageLayout<D>::offset(mb * 32 + col, 2 * ks + hf));
+            kbuf(buf, mb >> 1) + PageLayout<D>::offset((mb & 1) * 32 + col, 2 * ks + hf));
         sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, a), qf[ks], ks == 0 ? (f32x16_t){} : sacc[mb], 0, 0,
             0);
@@ -321,10 +361,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     }
   };
   // P = exp2(S * scale_log2 - mu) rounded to bf16 (the P^T operand), row sum
-  auto softmax_p = [&](const f32x16_t (&sacc)[2], float mu, bf16x8_t (&pb)[4]) -> float {
+  auto softmax_p = [&](const f32x16_t (&sacc)[MB], float mu, bf16x8_t (&pb)[2 * MB]) -> float {
     float part = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mb][r], c2, -mu));
@@ -354,16 +394,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       }
     }
   }
-  auto pv = [&](const unsigned char* vb, const bf16x8_t (&pb)[4]) {
+  auto pv = [&](int buf, const bf16x8_t (&pb)[2 * MB]) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 4 * PPB; ++ks) {
+      const unsigned char* vb = vbuf_of(buf, ks >> 2);
 #pragma unroll
       for (int md = 0; md < DBLK; ++md) {
         u32x4_t a;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4i16_t*)(vb + vtr[r][md] + ks * (32 * D)));
+              (__attribute__((address_space(3))) v4i16_t*)(vb + vtr[r][md] +
+                                                            (ks & 3) * (32 * D)));
           const u32x2_t w = __builtin_bit_cast(u32x2_t, v);
           a[2 * r] = w[0];
           a[2 * r + 1] = w[1];
@@ -373,21 +415,27 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
       }
     }
   };
-  // Key rows past the end of the sequence on its last page may hold anything
-  // (P is 0 there, but 0 * NaN is not): zero them in the V page before P V.
-  auto zero_v_tail = [&](unsigned char* vb, int valid_keys) {
+  // Key rows past the end of the sequence in its last block may hold anything
+  // (P is 0 there, but 0 * NaN is not; a page past the end was not copied):
+  // zero them in the V pages before P V.
+  auto zero_v_tail = [&](int buf, int valid_keys) {
     constexpr int kRowChunks = D / 8;
-    for (int f = valid_keys * kRowChunks + tid; f < kPage * kRowChunks; f += NT)
-      *reinterpret_cast<u32x4_t*>(vb + f * 16) = (u32x4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s = 0; s < PPB; ++s) {
+      const int valid = min(max(valid_keys - s * kPage, 0), kPage);
+      unsigned char* vb = vbuf_of(buf, s);
+      for (int f = valid * kRowChunks + tid; f < kPage * kRowChunks; f += NT)
+        *reinterpret_cast<u32x4_t*>(vb + f * 16) = (u32x4_t){0u, 0u, 0u, 0u};
+    }
   };
-  // causal / end-of-sequence mask (diagonal and tail pages only), then the
+  // causal / end-of-sequence mask (diagonal and tail blocks only), then the
   // row's block max in log2 units
-  auto mask_max = [&](int block, f32x16_t (&sacc)[2]) -> float {
-    const int key0 = block * kPage;
-    if ((key0 + kPage - 1 > wave_q0) || (key0 + kPage > L)) {
+  auto mask_max = [&](int block, f32x16_t (&sacc)[MB]) -> float {
+    const int key0 = block * KVB;
+    if ((key0 + KVB - 1 > wave_q0) || (key0 + KVB > L)) {
       const int lim = min(qpos, L - 1) - key0 - 4 * hf;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int koff = mb * 32 + 8 * (r >> 2) + (r & 3);
@@ -396,7 +444,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
     return pair_max(mx) * c2;
@@ -409,33 +457,33 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     }
   };
 
-  // Page loop, one workgroup barrier per visited page.  Iteration t: S(t)
-  // from the K page already in LDS, mask, block max and the tile vote;
-  // barrier (every copy issued so far has landed); read the vote; start the
-  // copies of K(t+2) and V(t+1) (HBM -> LDS); then the softmax and P V of
-  // page t unless the tile skips it.
+  // Block loop, one workgroup barrier per visited logical block.  Iteration
+  // t: S(t) from the K pages already in LDS, mask, block max and the tile
+  // vote; barrier (every copy issued so far has landed); read the vote; start
+  // the copies of K(t+2) and V(t+1) (HBM -> LDS); then the softmax and P V of
+  // block t unless the tile skips it.
   int j_cur = 0, j_next = 0;
   if (cnt > 0) {
     j_cur = slot_block(0);
-    if (selected(0)) copy_k(slot_page(0), 0);
+    if (selected(0)) copy_k(0, j_cur, 0);
     if (cnt > 1) {
       j_next = slot_block(1);
-      if (selected(1)) copy_k(slot_page(1), 1);
+      if (selected(1)) copy_k(1, j_next, 1);
     }
-    if (selected(0)) copy_v(slot_page(0), 0);
+    if (selected(0)) copy_v(0, j_cur, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   for (int t = 0; t < cnt; ++t) {
     const int buf = t & 1;
-    const int key0 = j_cur * kPage;
+    const int key0 = j_cur * KVB;
     const bool sel = selected(t);
-    // some key of the page is visible to some valid row of this wave
+    // some key of the block is visible to some valid row of this wave
     const bool active = sel && wave_has_rows && key0 <= wave_last;
-    f32x16_t sacc[2];
+    f32x16_t sacc[MB];
     float bm = kNegInf;
     if (active) {
-      qk(kbuf(buf), sacc);
+      qk(buf, sacc);
       bm = mask_max(j_cur, sacc);
     }
     vote(bm, buf);
@@ -457,15 +505,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
     // ---- prefetch: K(t+2) and V(t+1) straight into LDS, and the slot chunk
     // after the one that holds slot t+1
     advance_chunks(t + 1);
-    const int j_after = j_next;
+    const int j_after = j_next;   // block of slot t+1
     if (t + 2 < cnt) {
       j_next = slot_block(t + 2);
-      if (selected(t + 2)) copy_k(slot_page(t + 2), buf);
+      if (selected(t + 2)) copy_k(t + 2, j_next, buf);
     }
-    if (t + 1 < cnt && selected(t + 1)) copy_v(slot_page(t + 1), buf ^ 1);
+    if (t + 1 < cnt && selected(t + 1)) copy_v(t + 1, j_after, buf ^ 1);
 
-    if (sel && !skip && key0 + kPage > L) {   // uniform: the sequence's last page
-      zero_v_tail(vbuf_of(buf), L - key0);
+    if (sel && !skip && key0 + KVB > L) {   // uniform: the sequence's last block
+      zero_v_tail(buf, L - key0);
       __syncthreads();
     }
     if (active && !skip) {
@@ -482,9 +530,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
         for (int md = 0; md < DBLK; ++md) o[md] *= alpha;
       }
       const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
-      bf16x8_t pb[4];
+      bf16x8_t pb[2 * MB];
       lsum += softmax_p(sacc, mu, pb);
-      pv(vbuf_of(buf), pb);
+      pv(buf, pb);
     }
     j_cur = j_after;
   }
@@ -521,30 +569,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnParams p
   }
 }
 
-template <int D, int NW, int kMode>
+template <int D, int NW, int kMode, int PPB>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.batch * p.hq * p.nqb;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, kMode>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, kMode, PPB>), dim3((unsigned)grid), dim3(NW * 64),
+                     0, stream, p);
   return hipGetLastError();
+}
+
+template <int D, int NW>
+hipError_t launch_mode(const AttnParams& p, AttnMode mode, int ppb, hipStream_t stream) {
+  if (ppb == 2) {
+    if (mode == kModeOrdered) return launch_one<D, NW, kModeOrdered, 2>(p, stream);
+    if (mode == kModeDense) return launch_one<D, NW, kModeDense, 2>(p, stream);
+    return hipErrorInvalidValue;
+  }
+  if (mode == kModeOrdered) return launch_one<D, NW, kModeOrdered, 1>(p, stream);
+  if (mode == kModeLogical) return launch_one<D, NW, kModeLogical, 1>(p, stream);
+  return launch_one<D, NW, kModeDense, 1>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, AttnMode mode,
                             hipStream_t stream) {
-#define COSA_ATTN_CASE(D_, BQ_)                                                       \
-  if (head_dim == D_ && q_block == BQ_) {                                             \
-    if (mode == kModeOrdered) return launch_one<D_, BQ_ / 32, kModeOrdered>(p, stream); \
-    if (mode == kModeLogical) return launch_one<D_, BQ_ / 32, kModeLogical>(p, stream); \
-    return launch_one<D_, BQ_ / 32, kModeDense>(p, stream);                           \
-  }
-  COSA_ATTN_CASE(128, 128)
-  COSA_ATTN_CASE(128, 64)
-  COSA_ATTN_CASE(64, 128)
-  COSA_ATTN_CASE(64, 64)
-#undef COSA_ATTN_CASE
+  if (head_dim == 128 && q_block == 128) return launch_mode<128, 4>(p, mode, p.ppb, stream);
+  if (head_dim == 128 && q_block == 64) return launch_mode<128, 2>(p, mode, p.ppb, stream);
+  if (head_dim == 64 && q_block == 128) return launch_mode<64, 4>(p, mode, p.ppb, stream);
+  if (head_dim == 64 && q_block == 64) return launch_mode<64, 2>(p, mode, p.ppb, stream);
   return hipErrorInvalidValue;
 }
 

@@ -51,12 +51,14 @@ cosa_status validate(const cosa_problem* p) {
   if (p->q_block != 64 && p->q_block != 128)
     return fail(COSA_ERR_UNSUPPORTED, "q_block must be 64 or 128");
   if (p->page_size != cosa::kPage) return fail(COSA_ERR_UNSUPPORTED, "page_size must be 64");
-  if (p->kv_block != p->page_size)
-    return fail(COSA_ERR_UNSUPPORTED, "kv_block must equal page_size");
+  if (p->kv_block != p->page_size && p->kv_block != 2 * p->page_size)
+    return fail(COSA_ERR_UNSUPPORTED, "kv_block must be page_size or 2 * page_size");
   if (p->max_seqlen < 1 || p->max_seqlen > (1 << 20))
     return fail(COSA_ERR_INVALID_ARG, "max_seqlen must lie in [1, 2^20]");
-  if (p->max_pages_per_seq < ceil_div(p->max_seqlen, p->page_size))
-    return fail(COSA_ERR_INVALID_ARG, "max_pages_per_seq < ceil(max_seqlen / page_size)");
+  if (p->max_pages_per_seq <
+      ceil_div(p->max_seqlen, p->kv_block) * (p->kv_block / p->page_size))
+    return fail(COSA_ERR_INVALID_ARG,
+                "max_pages_per_seq < ceil(max_seqlen / kv_block) * (kv_block / page_size)");
   if (p->num_pages < 1) return fail(COSA_ERR_INVALID_ARG, "num_pages must be >= 1");
   if (p->total_q < 0 || p->total_q > (int64_t)p->batch * p->max_seqlen)
     return fail(COSA_ERR_INVALID_ARG, "total_q must lie in [0, batch * max_seqlen]");
@@ -94,6 +96,7 @@ void fill_attn(cosa::AttnParams& a, const cosa_problem* p, const void* q, const 
   a.skip_record = nullptr;
   a.row_stats = nullptr;
   a.mask_heads = p->num_q_heads;
+  a.ppb = p->kv_block / p->page_size;
   a.block_mask = nullptr;
   a.mask_words = 0;
   a.capacity = 0;
@@ -394,6 +397,8 @@ COSA_EXPORT cosa_status cosa_block_mask_prefill(const cosa_problem* p, const voi
   if (q == nullptr || k_pool == nullptr || v_pool == nullptr || out == nullptr ||
       block_mask == nullptr)
     return fail(COSA_ERR_INVALID_ARG, "q, k_pool, v_pool, block_mask and out are required");
+  if (p->kv_block != p->page_size)
+    return fail(COSA_ERR_UNSUPPORTED, "logical mask skipping needs kv_block == page_size");
   if (mask_words < ceil_div(ceil_div(p->max_seqlen, p->kv_block), 32))
     return fail(COSA_ERR_INVALID_ARG, "mask_words < ceil(ceil(max_seqlen / kv_block) / 32)");
   cosa::AttnParams a;

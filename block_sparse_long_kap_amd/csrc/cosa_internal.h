@@ -35,6 +35,7 @@ struct AttnParams {
   uint8_t* skip_record;           // OSK only, nullable
   int32_t* row_stats;             // OSK only, nullable
   int32_t mask_heads;             // OSK: heads of the mask layout (Hq, or Hkv when shared)
+  int32_t ppb;                    // pages per logical key block (1 or 2)
   const uint32_t* block_mask;     // logical-skip mode only: [rows][mask_words] bits
   int64_t mask_words;
   int64_t capacity;

@@ -13,7 +13,7 @@ from .api import OrderedMask, Problem
 def block_bitmask(problem: Problem, mask: OrderedMask) -> torch.Tensor:
     """int32 [B][Hq][NQB][words] bitmask (uint32 bit patterns) of the blocks an
     ordered mask keeps: bit j % 32 of word j / 32 is set iff block j is listed."""
-    n_max = -(-problem.max_seqlen // problem.page_size)
+    n_max = -(-problem.max_seqlen // problem.kv_block)
     words = -(-n_max // 32)
     rows = tuple(mask.blocks.shape[:-1])
     blocks = mask.blocks.long()

@@ -60,6 +60,8 @@ class Workload:
     outlier_scale: float = 10.0
     # extra query/key pushes used only by test variants
     q_dir_gain: float = 1.0
+    # logical key block of the sparse path (None: one page)
+    kv_block: Optional[int] = None
     budgets_sweep: Tuple[float, ...] = ()
     taus_sweep: Tuple[float, ...] = ()
 
@@ -74,6 +76,11 @@ class Workload:
     @property
     def max_seqlen(self) -> int:
         return int(max(self.seqlens)) if self.seqlens else 0
+
+    @property
+    def block(self) -> int:
+        """Tokens per logical key block."""
+        return self.page_size if self.kv_block is None else self.kv_block
 
     @property
     def softmax_scale(self) -> float:

@@ -191,7 +191,9 @@ def make(w: Workload, seed: Optional[int] = None) -> Inputs:
     used = int(sum(npages))
     P = used + w.spare_pages
     perm = rp.permutation(P) if w.shuffled_pages else np.arange(P)
-    max_pages = max(npages) if npages else 0
+    # page-table rows cover whole logical blocks (unused entries stay -1)
+    per_block = w.block // PG
+    max_pages = max(-(-n // per_block) * per_block for n in npages) if npages else 0
     page_table = np.full((B, max(max_pages, 1)), -1, dtype=np.int32)
     k_pool = np.full((P, Hkv, PG, D), np.nan, dtype=np.float32)
     v_pool = np.full((P, Hkv, PG, D), np.nan, dtype=np.float32)

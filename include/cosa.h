@@ -66,10 +66,11 @@ typedef struct {
   int32_t num_kv_heads;      /* Hkv >= 1                                   */
   int32_t head_dim;          /* 64 or 128                                  */
   int32_t q_block;           /* query tile rows: 64 or 128                 */
-  int32_t kv_block;          /* logical key block: must equal page_size    */
+  int32_t kv_block;          /* logical key block: page_size or 2*page_size */
   int32_t page_size;         /* tokens per KV page: 64                     */
   int32_t max_seqlen;        /* >= every sequence length, <= 1 << 20       */
-  int32_t max_pages_per_seq; /* page_table row stride, >= ceil(max_seqlen / page_size) */
+  int32_t max_pages_per_seq; /* page_table row stride, >= ceil(max_seqlen / kv_block)
+                                * (kv_block / page_size)                    */
   int32_t num_pages;         /* pages in the pool                          */
   int64_t total_q;           /* cu_seqlens[batch]                          */
   float softmax_scale;       /* > 0, usually 1/sqrt(head_dim)              */
@@ -134,7 +135,12 @@ cosa_status cosa_check_page_table_host(const cosa_problem* p, const int32_t* cu_
  *
  * Outputs (device, int32, per mask row; slots past the count are set to -1):
  *   ordered_blocks [rows][capacity]  logical key block ids in visiting order
- *   ordered_pages  [rows][capacity]  page_table[b][ordered_blocks[...]]
+ *   ordered_pages  [rows][capacity * P]  the P = kv_block / page_size pages
+ *                                    of each listed block: entry t * P + s is
+ *                                    page_table[b][ordered_blocks[t] * P + s],
+ *                                    -1 for a page past the sequence's end
+ *                                    (a logical block resolved through one or
+ *                                    more physical pages, pp App. D.1)
  *   counts         [rows]            k (0 for tiles past a sequence's end)
  *   hrm_counts     [rows] nullable   number of HRM blocks among the kept ones
  *                                    (they are its first hrm_counts slots)
@@ -203,8 +209,9 @@ cosa_status cosa_proxy_ordered_mask_shared_kv(const cosa_problem* p, const void*
  * Ordered-Skipping Kernel (CoSA (paperpeel) §4.3, App. D.1; skip rule §3.3).
  *
  * For every mask row (b, h, i) the kernel walks slots t = 0..counts[row]-1 in
- * order, fetching key/value page ordered_pages[row][t] (logical block
- * ordered_blocks[row][t], used for the causal mask), forms the exact logits
+ * order, fetching the key/value pages ordered_pages[row][t * P .. t * P + P-1]
+ * (P = kv_block / page_size; the pages of logical block
+ * ordered_blocks[row][t], which gives the causal mask), forms the exact logits
  * S = softmax_scale * Q K^T of the tile, and keeps the online-softmax running
  * max m and sum l per query row.  If skip_tau >= 0 and every valid row r of
  * the tile has max_c S[r][c] < m_r - skip_tau (the running max before the
@@ -221,7 +228,9 @@ cosa_status cosa_proxy_ordered_mask_shared_kv(const cosa_problem* p, const void*
  *            skipped in-kernel, 0 if computed; slots past the count untouched.
  * row_stats  device int32 [rows][2] nullable: (visited slots, skipped slots).
  * Every listed block id must lie in [0, ceil(L_b / kv_block)) for its
- * sequence and every page id in [0, num_pages).
+ * sequence and every page id of a page holding keys of the sequence in
+ * [0, num_pages).  With kv_block = 2 * page_size the vote and the skip cover
+ * the whole 128-key logical block (the pages' b = 128, App. D.1).
  */
 cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* ordered_blocks,

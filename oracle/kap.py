@@ -211,7 +211,7 @@ def group_tiles(q_heads, k_g: np.ndarray, scale: float, q_block: int, kv_block: 
 @dataclass
 class OrderedMask:
     blocks: np.ndarray      # int32 [B][Hq][NQBmax][C], -1 past count
-    pages: np.ndarray       # int32 [B][Hq][NQBmax][C], -1 past count
+    pages: np.ndarray       # int32 [B][Hq][NQBmax][C * kv_block / page], -1 past count
     counts: np.ndarray      # int32 [B][Hq][NQBmax]
     hrm_counts: np.ndarray  # int32 [B][Hq][NQBmax]
     capacity: int
@@ -240,13 +240,14 @@ def proxy_ordered_mask(q: np.ndarray, k_pool: np.ndarray, page_table: np.ndarray
     C = mask_capacity(max_len, kv_block, beta_ppm)
     H = num_kv_heads if shared_kv else Hq
     blocks = np.full((B, H, nqb_max, C), -1, dtype=np.int32)
-    pages = np.full((B, H, nqb_max, C), -1, dtype=np.int32)
+    page_size = k_pool.shape[2]
+    if kv_block % page_size != 0:
+        raise ValueError("a logical key block must span whole pages")
+    ppb = kv_block // page_size
+    pages = np.full((B, H, nqb_max, C * ppb), -1, dtype=np.int32)
     counts = np.zeros((B, H, nqb_max), dtype=np.int32)
     hrm_counts = np.zeros((B, H, nqb_max), dtype=np.int32)
     tiles = {}
-    page_size = k_pool.shape[2]
-    if page_size != kv_block:
-        raise ValueError("the ordered mask maps one key block to one page")
     for b, start, L in sequence_slices(cu_seqlens):
         if L == 0:
             continue
@@ -264,7 +265,10 @@ def proxy_ordered_mask(q: np.ndarray, k_pool: np.ndarray, page_table: np.ndarray
             for i, tp in res.items():
                 kk = tp.k
                 blocks[b, h, i, :kk] = tp.blocks
-                pages[b, h, i, :kk] = page_table[b][tp.blocks]
+                for t, j in enumerate(tp.blocks):
+                    for e in range(ppb):   # pages of the block that hold keys
+                        if j * kv_block + e * page_size < L:
+                            pages[b, h, i, t * ppb + e] = page_table[b][j * ppb + e]
                 counts[b, h, i] = kk
                 hrm_counts[b, h, i] = tp.hrm_count
                 tiles[(b, h, i)] = tp

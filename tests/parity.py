@@ -42,7 +42,7 @@ def upload(x, device, q_block=None):
                    num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                    max_seqlen=int(max(w.seqlens)), total_q=int(x.cu_seqlens[-1]),
                    num_pages=x.k_pool.shape[0], q_block=q_block or w.q_block,
-                   page_size=w.page_size, softmax_scale=w.softmax_scale)
+                   page_size=w.page_size, softmax_scale=w.softmax_scale, kv_block=w.block)
     return prob, q, k, v
 
 
@@ -89,18 +89,31 @@ def _hrm_sets(tile: TileProxy, gap: float):
     return certain, possible
 
 
+def expected_pages(blocks, page_table_row, ppb=1, kv_block=None, L=None):
+    """The page list of an ordered block list: P = ppb pages per block, -1 for
+    a page past the sequence's end."""
+    out = []
+    for j in np.asarray(blocks, dtype=np.int64):
+        for e in range(ppb):
+            ok = ppb == 1 or j * kv_block + e * (kv_block // ppb) < L
+            out.append(int(page_table_row[j * ppb + e]) if ok else -1)
+    return np.asarray(out, dtype=np.int64)
+
+
 def check_kap_row(gpu_blocks, gpu_pages, gpu_count, gpu_hrm_count, tile: TileProxy,
-                  page_table_row, w_rtol=W_RTOL, gap=HRM_GAP) -> str:
+                  page_table_row, w_rtol=W_RTOL, gap=HRM_GAP, ppb=1, kv_block=None,
+                  L=None) -> str:
     """'exact' if the row equals the oracle's, 'tie' if it differs only where
     the oracle's own scores are within the near-tie tolerances; raises
-    AssertionError otherwise."""
+    AssertionError otherwise.  ``gpu_pages`` holds ppb pages per slot."""
     k = tile.k
     C = len(gpu_blocks)
     assert int(gpu_count) == k, f"count {gpu_count} != {k}"
     g = np.asarray(gpu_blocks[:k], dtype=np.int64)
     assert np.all(np.asarray(gpu_blocks[k:]) == -1), "slots past the count must be -1"
-    assert np.all(np.asarray(gpu_pages[k:]) == -1), "pages past the count must be -1"
-    assert np.array_equal(np.asarray(gpu_pages[:k]), page_table_row[g]), "page remap mismatch"
+    assert np.all(np.asarray(gpu_pages[k * ppb:]) == -1), "pages past the count must be -1"
+    assert np.array_equal(np.asarray(gpu_pages[:k * ppb]),
+                          expected_pages(g, page_table_row, ppb, kv_block, L)), "page remap mismatch"
     assert C >= k
     if np.array_equal(g, tile.blocks) and int(gpu_hrm_count) == tile.hrm_count:
         return "exact"

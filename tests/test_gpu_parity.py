@@ -18,7 +18,7 @@ from oracle import kap as okap
 from oracle import osk as oosk
 from oracle.paging import materialise
 
-from .parity import ErrStats, check_kap_row, check_osk_tile, upload
+from .parity import ErrStats, check_kap_row, check_osk_tile, expected_pages, upload
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -86,10 +86,15 @@ def _run_osk_vs_oracle(w, x, blocks, counts, tau, label, tiles=None, delta=None,
     ``shared`` the masks are per KV head (cosa_osk_prefill_shared_kv)."""
     prob, q, k, v = upload(x, DEV)
     C = blocks.shape[-1]
-    pages = np.where(blocks >= 0, 0, -1).astype(np.int32)
+    ppb = w.block // w.page_size
+    pages = np.full(blocks.shape[:-1] + (C * ppb,), -1, dtype=np.int32)
     for b in range(w.batch):
-        sel = blocks[b] >= 0
-        pages[b][sel] = x.page_table[b][blocks[b][sel]]
+        L_ = int(x.seqlens[b])
+        for idx in np.ndindex(*blocks.shape[1:-1]):
+            row = blocks[(b,) + idx]
+            n_ = int((row >= 0).sum())
+            pages[(b,) + idx][:n_ * ppb] = expected_pages(row[:n_], x.page_table[b], ppb,
+                                                          w.block, L_)
     mask = bk.OrderedMask(blocks=torch.from_numpy(blocks).to(DEV),
                           pages=torch.from_numpy(pages).to(DEV),
                           counts=torch.from_numpy(counts).to(DEV), hrm_counts=None, capacity=C)
@@ -130,10 +135,10 @@ def _run_osk_vs_oracle(w, x, blocks, counts, tau, label, tiles=None, delta=None,
                 bl = blocks[b, h, i, :cnt]
                 qr = x.q[s0 + rows, h].astype(np.float64)
                 r = oosk.osk_tile_closed_form(qr, rows, kk[:, g], vv[:, g], bl, tau_b,
-                                              w.softmax_scale, w.page_size, skip_on=on)
+                                              w.softmax_scale, w.block, skip_on=on)
                 near_total += check_osk_tile(out[s0 + rows, h], lse[h, s0 + rows],
                                              rec[b, h, i], r, qr, rows, kk[:, g], vv[:, g], bl,
-                                             w.softmax_scale, w.page_size, st, ls)
+                                             w.softmax_scale, w.block, st, ls)
                 n_skipped += int(rec[b, h, i, :cnt].sum())
                 assert stats[b, h, i, 0] == cnt
                 assert stats[b, h, i, 1] == int(rec[b, h, i, :cnt].sum())
@@ -148,7 +153,7 @@ def test_osk_full_budget_skip_off_equals_dense(case):
     name, kw = case
     w, x = _inputs(name, **kw)
     print(f"[case] osk full budget {name} {kw}", flush=True)
-    blocks, counts = oosk.dense_order_mask(x.cu_seqlens, w.num_q_heads, w.q_block, w.page_size)
+    blocks, counts = oosk.dense_order_mask(x.cu_seqlens, w.num_q_heads, w.q_block, w.block)
     _run_osk_vs_oracle(w, x, blocks, counts, -1.0, f"osk-full {name}")
 
 
@@ -157,7 +162,7 @@ def test_osk_oracle_mask_with_skip(tau):
     w, x = _inputs("tiny_skip")
     print(f"[case] osk tiny_skip tau={tau}", flush=True)
     m = okap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
-                                w.q_block, w.page_size, w.budget, w.softmax_scale)
+                                w.q_block, w.block, w.budget, w.softmax_scale)
     n = _run_osk_vs_oracle(w, x, m.blocks, m.counts, tau, f"osk tiny_skip tau={tau}")
     if 0 <= tau <= 8:
         assert n > 0
@@ -167,7 +172,7 @@ def test_osk_any_order_same_output():
     # reversed and shuffled visiting orders of the same set, skip off
     w, x = _inputs("tiny", **RAGGED)
     print("[case] osk any-order", flush=True)
-    blocks, counts = oosk.dense_order_mask(x.cu_seqlens, w.num_q_heads, w.q_block, w.page_size)
+    blocks, counts = oosk.dense_order_mask(x.cu_seqlens, w.num_q_heads, w.q_block, w.block)
     rng = np.random.default_rng(0)
     sh = blocks.copy()
     for idx in np.ndindex(*counts.shape):
@@ -180,7 +185,7 @@ def test_osk_ragged_small_budget_with_kap_order():
     w, x = _inputs("tiny", **dict(RAGGED, q_dir_gain=6.0))
     print("[case] osk ragged budget 0.2", flush=True)
     m = okap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
-                                w.q_block, w.page_size, 0.2, w.softmax_scale)
+                                w.q_block, w.block, 0.2, w.softmax_scale)
     _run_osk_vs_oracle(w, x, m.blocks, m.counts, 2.0, "osk ragged b=0.2 tau=2")
 
 
@@ -190,7 +195,7 @@ def _kap_compare(w, x, budget, label, tiles=None, debug=True):
     torch.cuda.synchronize()
     gb, gp, gc, gh = _np(gm.blocks), _np(gm.pages), _np(gm.counts), _np(gm.hrm_counts)
     beta = okap.budget_ppm(budget)
-    assert gm.capacity == okap.mask_capacity(int(max(w.seqlens)), w.page_size, beta)
+    assert gm.capacity == okap.mask_capacity(int(max(w.seqlens)), w.block, beta)
     exact = ties = 0
     grp = w.num_q_heads // w.num_kv_heads
     for b in range(w.batch):
@@ -206,10 +211,11 @@ def _kap_compare(w, x, budget, label, tiles=None, debug=True):
             if want is not None and not want:
                 continue
             res = okap.head_tiles(x.q[s0:s0 + L, h].astype(np.float64), kk[:, h // grp],
-                                  w.softmax_scale, w.q_block, w.page_size, beta, tiles=want)
+                                  w.softmax_scale, w.q_block, w.block, beta, tiles=want)
             for i, tile in res.items():
                 kind = check_kap_row(gb[b, h, i], gp[b, h, i], gc[b, h, i], gh[b, h, i], tile,
-                                     x.page_table[b])
+                                     x.page_table[b], ppb=w.block // w.page_size,
+                                     kv_block=w.block, L=L)
                 exact += kind == "exact"
                 ties += kind == "tie"
     print(f"[parity] {label}: KAP rows exact={exact} near-tie={ties}")
@@ -261,7 +267,7 @@ def test_osk_delta_per_sequence_threshold(delta):
     w, x = _inputs("tiny_skip", **SKIP_RAGGED)
     print(f"[case] osk delta={delta} seqlens={w.seqlens}", flush=True)
     m = okap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
-                                w.q_block, w.page_size, w.budget, w.softmax_scale)
+                                w.q_block, w.block, w.budget, w.softmax_scale)
     n = _run_osk_vs_oracle(w, x, m.blocks, m.counts, 0.0, f"osk delta={delta}", delta=delta)
     if delta > 0:
         assert n > 0
@@ -327,7 +333,7 @@ def test_kap_top_p_matches_oracle(case):
         kk = materialise(x.k_pool, x.page_table[b], L, w.page_size)
         for h in range(w.num_q_heads):
             res = okap.head_tiles(x.q[s0:s0 + L, h].astype(np.float64), kk[:, h // grp],
-                                  w.softmax_scale, w.q_block, w.page_size, beta, top_p=top_p)
+                                  w.softmax_scale, w.q_block, w.block, beta, top_p=top_p)
             for i, tile in res.items():
                 c = int(gc[b, h, i])
                 # 1) bit-exact: the documented rule on the kernel's own w and flags
@@ -357,7 +363,7 @@ def test_osk_ascending_order_of_kap_set_with_skip():
     w, x = _inputs("tiny_skip")
     print("[case] osk ascending kap set tau=4", flush=True)
     m = okap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
-                                w.q_block, w.page_size, w.budget, w.softmax_scale)
+                                w.q_block, w.block, w.budget, w.softmax_scale)
     asc = m.blocks.copy()
     for idx in np.ndindex(*m.counts.shape):
         c = m.counts[idx]
@@ -393,7 +399,7 @@ def test_block_mask_logical_skip_matches_oracle(case):
                 rows = np.arange(i * w.q_block, min((i + 1) * w.q_block, L))
                 key_ok = np.zeros(L, dtype=bool)
                 for j in gb[b, h, i, :gc[b, h, i]]:
-                    key_ok[j * w.page_size:min((j + 1) * w.page_size, L)] = True
+                    key_ok[j * w.block:min((j + 1) * w.block, L)] = True
                 o, l_ = odense.attention_rows(x.q[s0 + rows, h].astype(np.float64), rows,
                                               kk[:, h // grp], vv[:, h // grp], w.softmax_scale,
                                               key_ok=key_ok)
@@ -440,7 +446,7 @@ def test_kap_shared_kv_matches_oracle(case):
         kk = materialise(x.k_pool, x.page_table[b], L, w.page_size)
         for g in range(w.num_kv_heads):
             qs = [x.q[s0:s0 + L, h].astype(np.float64) for h in range(g * grp, (g + 1) * grp)]
-            res = okap.group_tiles(qs, kk[:, g], w.softmax_scale, w.q_block, w.page_size, beta,
+            res = okap.group_tiles(qs, kk[:, g], w.softmax_scale, w.q_block, w.block, beta,
                                    top_p=tp)
             for i, tile in res.items():
                 c = int(gc[b, g, i])
@@ -462,5 +468,58 @@ def test_osk_shared_kv_masks(tau):
     w, x = _inputs("tiny", **dict(RAGGED, q_dir_gain=6.0))
     print(f"[case] osk shared masks tau={tau}", flush=True)
     m = okap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
-                                w.q_block, w.page_size, 0.3, w.softmax_scale, shared_kv=True)
+                                w.q_block, w.block, 0.3, w.softmax_scale, shared_kv=True)
     _run_osk_vs_oracle(w, x, m.blocks, m.counts, tau, f"osk shared tau={tau}", shared=True)
+
+
+# ---------------------------------------------------------------------------
+# Logical key blocks of 128 keys resolved through two 64-token pages
+
+
+KV128 = dict(RAGGED, kv_block=128, seqlens=(1, 63, 64, 65, 127, 128, 129, 200, 383))
+
+
+def test_dense_kv_block_128_matches_oracle():
+    w, x = _inputs("tiny", **KV128)
+    print("[case] dense kv_block=128", flush=True)
+    prob, q, k, v = upload(x, DEV)
+    res = bk.dense_prefill(prob, q, k, v)
+    torch.cuda.synchronize()
+    ref, ref_lse = _dense_oracle(x, w)
+    st, ls = ErrStats(), ErrStats()
+    st.add(_np(res.out), ref)
+    ls.add(_np(res.lse), ref_lse)
+    st.assert_ok(label="dense kv_block=128 out")
+    ls.assert_ok(max_abs=1e-3, mean_abs=1e-4, label="dense kv_block=128 lse")
+
+
+def test_osk_kv_block_128_full_budget_and_shuffled():
+    w, x = _inputs("tiny", **KV128)
+    print("[case] osk kv_block=128 full budget, shuffled", flush=True)
+    blocks, counts = oosk.dense_order_mask(x.cu_seqlens, w.num_q_heads, w.q_block, w.block)
+    _run_osk_vs_oracle(w, x, blocks, counts, -1.0, "osk kv128 full")
+    rng = np.random.default_rng(1)
+    sh = blocks.copy()
+    for idx in np.ndindex(*counts.shape):
+        c = counts[idx]
+        sh[idx][:c] = rng.permutation(sh[idx][:c])
+    _run_osk_vs_oracle(w, x, sh, counts, -1.0, "osk kv128 shuffled")
+
+
+@pytest.mark.parametrize("budget", [0.3, 1.0])
+def test_kap_kv_block_128_matches_oracle(budget):
+    w, x = _inputs("tiny", **KV128)
+    print(f"[case] kap kv_block=128 budget={budget}", flush=True)
+    _, exact, ties = _kap_compare(w, x, budget, f"kap kv128 b={budget}")
+    assert exact > 0 and ties <= max(1, exact // 100)
+
+
+@pytest.mark.parametrize("tau", [0.0, 4.0, 8.0])
+def test_osk_kv_block_128_with_skip(tau):
+    w, x = _inputs("tiny_skip", kv_block=128, seqlens=(700, 1500, 90), shuffled_pages=True,
+                   spare_pages=5, precision="bf16")
+    print(f"[case] osk kv_block=128 tiny_skip tau={tau}", flush=True)
+    m = okap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
+                                w.q_block, w.block, w.budget, w.softmax_scale)
+    n = _run_osk_vs_oracle(w, x, m.blocks, m.counts, tau, f"osk kv128 tau={tau}")
+    assert n > 0

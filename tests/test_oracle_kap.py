@@ -281,3 +281,23 @@ def test_gqa_shared_equals_per_head_for_one_head_groups():
     assert w_.num_q_heads == w_.num_kv_heads
     for f in ("blocks", "pages", "counts", "hrm_counts"):
         assert np.array_equal(getattr(a, f), getattr(b, f))
+
+
+def test_two_page_logical_blocks_remap_pages():
+    """kv_block = 2 pages: every kept block lists its two pages (page table
+    entries 2j, 2j+1), and -1 for a second page past the sequence's end."""
+    w = ci.get("tiny").with_(seqlens=(129, 200, 64), kv_block=128, shuffled_pages=True,
+                             spare_pages=3)
+    x = ci.make(w)
+    m = kap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
+                               w.q_block, 128, 1.0, w.softmax_scale)
+    assert m.pages.shape[-1] == 2 * m.blocks.shape[-1]
+    for b, L in enumerate(w.seqlens):
+        for idx in np.ndindex(*m.counts.shape[1:]):
+            c = m.counts[(b,) + idx]
+            for t in range(c):
+                j = m.blocks[(b,) + idx][t]
+                p0, p1 = m.pages[(b,) + idx][2 * t:2 * t + 2]
+                assert p0 == x.page_table[b][2 * j]
+                assert p1 == (x.page_table[b][2 * j + 1] if 128 * j + 64 < L else -1)
+            assert np.all(m.pages[(b,) + idx][2 * c:] == -1)
