@@ -60,7 +60,11 @@ BAD = [
     (dict(head_dim=96), _lib.COSA_ERR_UNSUPPORTED),
     (dict(q_block=32), _lib.COSA_ERR_UNSUPPORTED),
     (dict(page_size=16, kv_block=16), _lib.COSA_ERR_UNSUPPORTED),
-    (dict(kv_block=128), _lib.COSA_ERR_UNSUPPORTED),
+    (dict(kv_block=192), _lib.COSA_ERR_UNSUPPORTED),
+    (dict(kv_block=32), _lib.COSA_ERR_UNSUPPORTED),
+    # two-page logical blocks need page-table rows covering whole blocks
+    (dict(kv_block=128, max_seqlen=130945, total_q=130945, max_pages_per_seq=2047),
+     _lib.COSA_ERR_INVALID_ARG),
     (dict(max_seqlen=0), _lib.COSA_ERR_INVALID_ARG),
     (dict(max_pages_per_seq=100), _lib.COSA_ERR_INVALID_ARG),
     (dict(num_pages=0), _lib.COSA_ERR_INVALID_ARG),
