@@ -306,42 +306,60 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   const uint16_t* kb_lo = kb_hi + plane;
   const int nb = (n_wg + 31) / 32;
 
-  // scores of candidate block cb for the 32 rows (log2 units)
-  auto scores = [&](int cb) -> f32x16_t {
+  // pooled-key operands of candidate block cb (B of the score product); a
+  // wave loads its next block right after the current block's products, so
+  // the loads travel while the row statistics are updated
+  bf16x8_t kh[KSTEPS], kl[KSTEPS];
+  auto load_ops = [&](int cb) {
     const int j = min(cb * 32 + col, nkb - 1);   // clamp reads; masked later
     const uint16_t* bh = kb_hi + (int64_t)j * D + hf * 8;
     const uint16_t* bl = kb_lo + (int64_t)j * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      kh[ks] = *reinterpret_cast<const bf16x8_t*>(bh + ks * 16);
+      kl[ks] = *reinterpret_cast<const bf16x8_t*>(bl + ks * 16);
+    }
+  };
+  // scores of the loaded block for the 32 rows (log2 units)
+  auto scores = [&]() -> f32x16_t {
     f32x16_t acc = {};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const bf16x8_t h8 = *reinterpret_cast<const bf16x8_t*>(bh + ks * 16);
-      const bf16x8_t l8 = *reinterpret_cast<const bf16x8_t*>(bl + ks * 16);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], h8, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], l8, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], h8, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], kh[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], kl[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], kh[ks], acc, 0, 0, 0);
     }
     return acc;
   };
+  // "have rowmax" flags as a bitmap per tile (in the radix histogram space,
+  // which is free until the selection)
+  uint32_t* sHrmBits = &sHist[0][0];   // [TPW][kMaxCandidates / 32]
+  static_assert(TPW * (kMaxCandidates / 32) <= NWAVE * 256, "bitmap fits");
+  for (int x = tid; x < TPW * (kMaxCandidates / 32); x += NT) sHrmBits[x] = 0u;
 
   // ---- 3) pass 1: per-row max, arg-max (lowest block) and sum, online
   RowStat st[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) st[r] = RowStat{kNegInf, 0.f, 0x7FFFFFFF};
+  if (wave < nb) load_ops(wave);
   for (int cb = wave; cb < nb; cb += NWAVE) {
-    const f32x16_t acc = scores(cb);
+    const f32x16_t acc = scores();
+    if (cb + NWAVE < nb) load_ops(cb + NWAVE);
     const int j = cb * 32 + col;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      if (j < cand[r]) {
-        const float s = acc[r];
-        if (s > st[r].m) {   // blocks arrive in ascending order per lane
-          st[r].z = st[r].z * (st[r].m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(st[r].m - s)) + 1.f;
-          st[r].m = s;
-          st[r].a = j;
-        } else {
-          st[r].z += __builtin_amdgcn_exp2f(s - st[r].m);
-        }
-      }
+      // one exponential per element: exp2(-|s - m|) rescales the sum when s
+      // raises the max (blocks arrive in ascending order per lane, so a
+      // strict raise keeps the lowest block index) and is s's term otherwise
+      const float s = acc[r];
+      const float d = s - st[r].m;            // +inf while the row is empty
+      const bool up = d > 0.f;
+      const float e = __builtin_amdgcn_exp2f(up ? -d : d);
+      const float zn = up ? fmaf(st[r].z, e, 1.f) : st[r].z + e;
+      const bool valid = j < cand[r];
+      st[r].z = valid ? zn : st[r].z;
+      st[r].a = valid && up ? j : st[r].a;
+      st[r].m = valid && up ? s : st[r].m;
     }
   }
   // merge over the 32 candidate lanes of each half, then over the waves
@@ -367,6 +385,10 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     sRowM[tid] = s.m;
     sRowInvZ[tid] = s.z > 0.f ? 1.f / s.z : 0.f;
     sRowA[tid] = s.m == kNegInf ? -1 : s.a;
+    if (s.m != kNegInf && tid < MR) {
+      const int t = tid / RPT;
+      atomicOr(&sHrmBits[t * (kMaxCandidates / 32) + (s.a >> 5)], 1u << (s.a & 31));
+    }
   }
   __syncthreads();
 
@@ -388,9 +410,7 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     unsigned long long key = ~0ull;
     if (j < n_t[t]) {
       const float w = wsum / (float)rows_t[t];
-      bool hrm = false;
-#pragma unroll
-      for (int r = 0; r < RPT; ++r) hrm |= (sRowA[t * RPT + r] == j);
+      const bool hrm = (sHrmBits[t * (kMaxCandidates / 32) + (j >> 5)] >> (j & 31)) & 1u;
       if (hrm) atomicAdd(&sHrm[t], 1);
       const uint32_t wb = __float_as_uint(w);   // w >= 0: bit order == value order
       key = ((unsigned long long)(hrm ? 0u : 1u) << 63) |
@@ -402,8 +422,10 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     if (j < npow) sKey[t][j] = key;
   };
 
+  if (wave < nb) load_ops(wave);
   for (int cb = wave; cb < nb; cb += NWAVE) {
-    const f32x16_t acc = scores(cb);
+    const f32x16_t acc = scores();
+    if (cb + NWAVE < nb) load_ops(cb + NWAVE);
     const int j = cb * 32 + col;
     float part[4];
 #pragma unroll
