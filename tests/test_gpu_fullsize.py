@@ -115,3 +115,50 @@ def test_full_layer_sampled_parity(name, n_samples):
     do.assert_ok(label=f"{name} dense out")
     dl.assert_ok(max_abs=1e-3, mean_abs=1e-4, label=f"{name} dense lse")
     assert kap_exact >= len(picks) // 2
+
+
+def test_full_layer_shared_kv_sampled_parity():
+    """llama128k with one mask per KV head (cosa_proxy_ordered_mask_shared_kv +
+    cosa_osk_prefill_shared_kv, as timed by bench.py --shared-kv), sampled."""
+    w = ci.get("llama128k")
+    print("[case] full-size shared-kv llama128k: generating inputs", flush=True)
+    x = ci.make(w).bf16_rounded()
+    prob, q, k, v = upload(x, DEV)
+    print("[case] full-size shared-kv llama128k: GPU layer", flush=True)
+    m = bk.proxy_ordered_mask_shared_kv(prob, q, k, w.budget)
+    r = bk.osk_prefill_shared_kv(prob, q, k, v, m, w.tau)
+    torch.cuda.synchronize()
+    gb, gp, gc, gh = _np(m.blocks), _np(m.pages), _np(m.counts), _np(m.hrm_counts)
+    out, lse, rec = _np(r.out), _np(r.lse), _np(r.skip_record)
+    del r, q, k, v
+    assert gb.shape[1] == w.num_kv_heads and np.all(np.isfinite(out))
+    beta = okap.budget_ppm(w.budget)
+    grp = w.num_q_heads // w.num_kv_heads
+    L = int(x.seqlens[0])
+    kk = materialise(x.k_pool, x.page_table[0], L, w.page_size)
+    vv = materialise(x.v_pool, x.page_table[0], L, w.page_size)
+    rng = np.random.default_rng(11)
+    nqb = (L + w.q_block - 1) // w.q_block
+    picks = sorted({(int(rng.integers(w.num_kv_heads)), int(rng.integers(nqb))) for _ in range(6)}
+                   | {(0, nqb - 1)})
+    so, sl = ErrStats(), ErrStats()
+    exact = near = 0
+    for g, i in picks:
+        qs = [x.q[:L, h].astype(np.float64) for h in range(g * grp, (g + 1) * grp)]
+        tile = okap.group_tiles(qs, kk[:, g], w.softmax_scale, w.q_block, w.page_size, beta,
+                                tiles=[i])[i]
+        exact += check_kap_row(gb[0, g, i], gp[0, g, i], gc[0, g, i], gh[0, g, i], tile,
+                               x.page_table[0]) == "exact"
+        bl = gb[0, g, i, :gc[0, g, i]]
+        rows = np.arange(i * w.q_block, min((i + 1) * w.q_block, L))
+        for h in (g * grp, g * grp + grp - 1):
+            qr = x.q[rows, h].astype(np.float64)
+            res = oosk.osk_tile_closed_form(qr, rows, kk[:, g], vv[:, g], bl, w.tau,
+                                            w.softmax_scale, w.page_size)
+            near += check_osk_tile(out[rows, h], lse[h, rows], rec[0, h, i], res, qr, rows,
+                                   kk[:, g], vv[:, g], bl, w.softmax_scale, w.page_size, so, sl)
+    print(f"[parity] shared-kv llama128k: KAP rows exact={exact} of {len(picks)}; "
+          f"near-threshold slots={near}")
+    so.assert_ok(label="shared-kv osk out")
+    sl.assert_ok(max_abs=1e-3, mean_abs=1e-4, label="shared-kv osk lse")
+    assert exact >= len(picks) // 2
