@@ -523,3 +523,40 @@ def test_osk_kv_block_128_with_skip(tau):
                                 w.q_block, w.block, w.budget, w.softmax_scale)
     n = _run_osk_vs_oracle(w, x, m.blocks, m.counts, tau, f"osk kv128 tau={tau}")
     assert n > 0
+
+
+# ---------------------------------------------------------------------------
+# Degenerate inputs: empty sequences in the batch, a budget that keeps one
+# block per tile, tau = 0, and every entry point on the same batch
+
+
+EMPTY = dict(seqlens=(0, 100, 0, 257, 1), num_q_heads=4, num_kv_heads=2, head_dim=64,
+             q_block=64, precision="bf16", shuffled_pages=True, spare_pages=3)
+
+
+def test_empty_sequences_and_single_block_budget():
+    w, x = _inputs("tiny", **EMPTY)
+    print("[case] empty sequences, budget keeping one block", flush=True)
+    prob, q, k, v = upload(x, DEV)
+    _, exact, ties = _kap_compare(w, x, 1e-6, "kap one block")
+    assert exact > 0 and ties == 0
+    gm = bk.proxy_ordered_mask(prob, q, k, 1e-6)
+    torch.cuda.synchronize()
+    gc = _np(gm.counts)
+    for b, L in enumerate(x.seqlens):
+        nqb = (int(L) + w.q_block - 1) // w.q_block
+        assert np.all(gc[b, :, :nqb] == 1) and np.all(gc[b, :, nqb:] == 0)
+    m = okap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
+                                w.q_block, w.block, 1e-6, w.softmax_scale)
+    _run_osk_vs_oracle(w, x, m.blocks, m.counts, 0.0, "osk one block tau=0")
+    # dense and shared masks on the same batch
+    res = bk.dense_prefill(prob, q, k, v)
+    torch.cuda.synchronize()
+    ref, ref_lse = _dense_oracle(x, w)
+    st = ErrStats()
+    st.add(_np(res.out), ref)
+    st.assert_ok(label="dense with empty sequences")
+    ms = okap.proxy_ordered_mask(x.q, x.k_pool, x.page_table, x.cu_seqlens, w.num_kv_heads,
+                                 w.q_block, w.block, 0.5, w.softmax_scale, shared_kv=True)
+    _run_osk_vs_oracle(w, x, ms.blocks, ms.counts, 4.0, "osk shared, empty sequences",
+                       shared=True)
