@@ -74,9 +74,13 @@ SIGNATURES = {
 _LIB = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load (once) and type the library; raise if it is not built."""
+def load(path: str = None) -> ctypes.CDLL:
+    """Load (once) and type the library; raise if it is not built.  The path
+    defaults to ``$COSA_LIBRARY`` if set (an alternative build of the same
+    sources), else the in-tree ``libcosa.so``."""
     global _LIB
+    if path is None:
+        path = os.environ.get("COSA_LIBRARY") or LIB_PATH
     if _LIB is not None:
         return _LIB
     if not os.path.exists(path):
