@@ -51,11 +51,19 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// The two 32-lane halves of a wavefront exchanged in one VALU instruction
+// (v_permlane32_swap): one of the returned values is the lane's own, the
+// other its partner's (lane ^ 32), so symmetric combinations need no order.
 __device__ __forceinline__ float pair_max(float x) {
-  // max over lanes l and l ^ 32
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // K and V pages in LDS: [64 keys][D] bf16 as in HBM, with the 16-byte
 // chunks of each row permuted by a function of the row.  Pages are copied
@@ -190,7 +198,9 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // uniform by construction; telling the compiler keeps the LDS destinations
+  // of the page copies in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5;
   const int col = lane & 31;
 
@@ -306,16 +316,23 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
   const int64_t page_stride = (int64_t)p.hkv * head_stride;
 
   // ---- K and V pages: HBM -> LDS without registers (16 bytes per lane per
-  // instruction)
+  // instruction).  Lane byte offsets inside a page are fixed for the kernel;
+  // the page's base is uniform.
+  uint32_t coff[K_PER];
+#pragma unroll
+  for (int e = 0; e < K_PER; ++e) {
+    const int f = e * NT + tid;                // physical 16-byte slot in the page
+    const int r = f / KCH;
+    const int c = (f % KCH) ^ PageLayout<D>::swz(r);
+    coff[e] = (uint32_t)(r * D + c * 8) * 2u;
+  }
   auto copy_page = [&](const uint16_t* pool, int page, unsigned char* dst) {
-    const uint16_t* base = pool + (int64_t)page * page_stride + (int64_t)g * head_stride;
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(
+        pool + (int64_t)page * page_stride + (int64_t)g * head_stride);
 #pragma unroll
     for (int e = 0; e < K_PER; ++e) {
-      const int f = e * NT + tid;              // physical 16-byte slot in the page
-      const int r = f / KCH;
-      const int c = (f % KCH) ^ PageLayout<D>::swz(r);
       __builtin_amdgcn_global_load_lds(
-          static_cast<const void*>(base + r * D + c * 8),
+          static_cast<const void*>(base + coff[e]),
           (__attribute__((address_space(3))) void*)(dst + (e * NT + wave * 64) * 16), 16, 0, 0);
     }
   };
@@ -474,8 +491,11 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  for (int t = 0; t < cnt; ++t) {
-    const int buf = t & 1;
+  // One step per slot; the slot's LDS buffer (t & 1) is a compile-time
+  // constant, so every LDS operand address is a fixed per-lane offset plus an
+  // immediate.
+  auto step = [&](const int t, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     const int key0 = j_cur * KVB;
     const bool sel = selected(t);
     // some key of the block is visible to some valid row of this wave
@@ -535,6 +555,10 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
       pv(buf, pb);
     }
     j_cur = j_after;
+  };
+  for (int t = 0; t < cnt; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < cnt) step(t + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: out = O / l, lse = m + ln l
