@@ -13,8 +13,11 @@
 // and the per-block barrier on the others (the logical mask skipping that
 // App. D.3 / Fig. B compares physical page jumping against).
 //
-// gfx950 mapping (one workgroup = one query tile of one query head):
-//   * NW wavefronts of 64 lanes, 32 query rows per wavefront (tile = 32*NW).
+// gfx950 mapping (one workgroup = one query tile of one query head, or of
+// two query heads of a KV group on the dense walk, which then share every K
+// and V page the workgroup loads):
+//   * NW wavefronts of 64 lanes per head, 32 query rows per wavefront
+//     (tile = 32*NW).
 //   * Logits are formed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: each lane then owns one query column and 32
 //     of the 64 keys of a page, so the row max is an in-register reduction
@@ -24,10 +27,12 @@
 //     is read from the page as stored ([key][D]) with the gfx950 transposing
 //     LDS read (ds_read_b64_tr_b16), in the key order the accumulator layout
 //     implies.
-//   * K and V pages are double-buffered in LDS and copied from HBM straight
-//     into LDS (no registers): K two pages ahead, V one page ahead.  One
-//     workgroup barrier per visited page carries both the LDS hand-off and
-//     the tile-wide skip vote.
+//   * K and V pages are copied from HBM straight into LDS (no registers)
+//     through a ring of NS stages: K NS pages ahead, V NS - 1 ahead (NS = 2
+//     with two workgroups per CU; NS = 4 for the two-head workgroup, alone on
+//     its CU).  One workgroup barrier per visited page carries both the LDS
+//     hand-off and the tile-wide skip vote; before it each wavefront waits
+//     only for its copies of the pages the next steps read.
 //   * Tile order: one (sequence, KV head) group at a time over the whole
 //     chip, longest tiles (most causal blocks) first inside the group, so the
 //     working set is that group's pages.  A level-major order and one that
@@ -38,6 +43,12 @@
 #include <type_traits>
 
 #include "cosa_internal.h"
+
+// Two query heads of a KV group per workgroup on the dense walk (0 turns the
+// pairing off).
+#ifndef COSA_HEAD_PAIRS
+#define COSA_HEAD_PAIRS 1
+#endif
 
 namespace cosa {
 namespace {
@@ -88,11 +99,13 @@ struct PageLayout {
   }
 };
 
-// Decode the workgroup's (sequence, head, tile).  Every order launches the
-// tiles with more causal blocks first (longest-processing-time first).
-__device__ __forceinline__ void decode_tile(const AttnParams& p, int bid, int& b, int& h,
+// Decode the workgroup's (sequence, head unit, tile).  A head unit is HP
+// consecutive query heads of one KV group; hq_u = Hq / HP units per sequence.
+// Every order launches the tiles with more causal blocks first
+// (longest-processing-time first).
+__device__ __forceinline__ void decode_tile(const AttnParams& p, int bid, int hq_u, int& b, int& h,
                                             int& i) {
-  const int hg = p.hq / p.hkv;
+  const int hg = hq_u / p.hkv;
   if (p.order == kOrderXcdGroup) {
     // consecutive workgroup ids go round-robin over the 8 XCDs: pin each
     // (sequence, KV head) group to one XCD so its pages stay in that L2
@@ -110,10 +123,10 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, int bid, int& b
     h = g * hg + hh;
     i = p.nqb - 1 - level;
   } else if (p.order == kOrderGroupXcd) {
-    // group-major sequence of (group, level) units, each unit's hg query
-    // heads on one XCD (workgroup ids go round-robin over the 8 XCDs): unit u
-    // runs on XCD u % 8, each XCD takes its units in sequence order, so the
-    // heads that share the group's pages share that XCD's L2
+    // group-major sequence of (group, level) units, each unit's head units on
+    // one XCD (workgroup ids go round-robin over the 8 XCDs): unit u runs on
+    // XCD u % 8, each XCD takes its units in sequence order, so the heads
+    // that share the group's pages share that XCD's L2
     const int x = bid & 7;
     const int r = bid >> 3;
     const int unit = (r / hg) * 8 + x;
@@ -138,30 +151,61 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, int bid, int& b
     h = g * hg + hh;
     i = p.nqb - 1 - level;
   } else {
-    const int per_level = p.batch * p.hq;
+    const int per_level = p.batch * hq_u;
     const int level = bid / per_level;
     const int rem = bid - level * per_level;
-    b = rem / p.hq;
-    h = rem - b * p.hq;
+    b = rem / hq_u;
+    h = rem - b * hq_u;
     i = p.nqb - 1 - level;
   }
 }
 
-// PPB = pages per logical key block (1: a 64-key block is one page; 2: a
-// 128-key block is resolved through two pages, with one vote per block).
-template <int D, int NW, int kMode, int PPB>
-__global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(const AttnParams p) {
+// s_waitcnt on the vector-memory count alone (export and LDS counts left at
+// their maxima): at most N of this wavefront's vector memory operations stay
+// outstanding.  They complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vm_c() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
+}
+
+// Workgroup barrier that orders LDS accesses (wait for this wavefront's LDS
+// operations, then s_barrier) but, unlike __syncthreads(), does not also wait
+// for the wavefront's HBM -> LDS copies still in flight; the memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Template parameters: D head dim; NW wavefronts per query head, 32 query
+// rows each (the tile is 32 NW rows of one head); kMode the page walk; PPB
+// pages per logical key block (1: a 64-key block is one page; 2: a 128-key
+// block is resolved through two pages, with one vote per block); HP query
+// heads per workgroup (2: two query heads of one KV group that walk the same
+// page list, dense or a mask shared by the KV group, compute on every K and V
+// page the workgroup loads, which halves the page traffic per query row); NS
+// LDS stages per operand (copies run NS blocks ahead for K and NS - 1 for V).
+template <int D, int NW, int kMode, int PPB, int HP, int NS>
+__global__ __launch_bounds__(NW * HP * 64, (PPB == 1 && HP == 1) ? 2 : 1) void attn_fwd_kernel(
+    const AttnParams p) {
   constexpr bool kOrdered = kMode == kModeOrdered;
   constexpr bool kLogical = kMode == kModeLogical;
   static_assert(PPB == 1 || PPB == 2, "one or two pages per logical block");
+  static_assert(HP == 1 || HP == 2, "one or two query heads per workgroup");
+  static_assert(NS == 2 || NS == 4, "two or four LDS stages");
+  static_assert(NS * PPB <= 4, "at most four LDS page buffers per operand");
+  static_assert(HP == 1 || !kLogical, "logical skipping walks one head per workgroup");
   constexpr int KVB = kPage * PPB;                   // keys per logical block
   constexpr int MB = 2 * PPB;                        // 32-key S^T blocks per logical block
-  constexpr int NT = NW * 64;
-  constexpr int BQ = NW * 32;
+  constexpr int NWT = NW * HP;                       // wavefronts per workgroup
+  constexpr int NT = NWT * 64;
+  constexpr int NTH = NW * 64;                       // threads per head
+  constexpr int BQ = NW * 32;                        // query rows per head (the tile)
   constexpr int KCH = D / 8;                         // 16-byte chunks per key row
   constexpr int K_TOTAL = kPage * KCH;               // 16-byte chunks per page
   static_assert(K_TOTAL % NT == 0, "page copy must split evenly over the workgroup");
   constexpr int K_PER = K_TOTAL / NT;
+  static_assert(NS == 2 || PPB == 1, "four stages hold one-page blocks");
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   // Lazy rescaling: the reference max used for the exponentials only moves
@@ -169,11 +213,12 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
   // accumulator is rarely rescaled; weights stay <= 2^kRescale.
   constexpr float kRescale = 8.f;
 
-  // Two buffers per operand as distinct LDS objects, so that the compiler
+  // Page buffers per operand as distinct LDS objects, so that the compiler
   // can tell reads of one buffer from the asynchronous HBM->LDS copies into
-  // the other and does not wait for those copies before the reads.
-  // Buffer (b, s) holds page s of the logical block in flight in slot b.
-  constexpr int kXtra = PPB == 2 ? PageLayout<D>::kBytes : 16;
+  // another and does not wait for those copies before the reads.
+  // Buffer stage * PPB + s holds page s of the logical block of that stage.
+  constexpr int kNB = NS * PPB;
+  constexpr int kXtra = kNB == 4 ? PageLayout<D>::kBytes : 16;
   __shared__ __attribute__((aligned(16))) unsigned char sK0[PageLayout<D>::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char sK1[PageLayout<D>::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char sK2[kXtra];
@@ -182,38 +227,45 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
   __shared__ __attribute__((aligned(16))) unsigned char sV1[PageLayout<D>::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char sV2[kXtra];
   __shared__ __attribute__((aligned(16))) unsigned char sV3[kXtra];
-  __shared__ int sVote[2][NW];
+  __shared__ int sVote[2][NWT];
   __shared__ int sSlotP[2][64 * PPB];   // [ring chunk][slot * PPB + page]
   __shared__ int sSlotB[2][64];         // [ring chunk][slot]: logical block
   // logical-skip mode: the tile's block bitmask (up to 16384 causal blocks)
   __shared__ uint32_t sBits[kLogical ? 512 : 1];
-  auto kbuf = [&](int buf, int s) -> unsigned char* {
-    const int x = buf * PPB + s;
+  // ordered mode: each head's skip decisions, one bit per slot (up to 16384)
+  __shared__ uint32_t sRec[kOrdered ? HP : 1][kOrdered ? 512 : 1];
+  auto kbuf = [&](int stage, int s) -> unsigned char* {
+    const int x = stage * PPB + s;
     return x == 0 ? sK0 : x == 1 ? sK1 : x == 2 ? sK2 : sK3;
   };
-  auto vbuf_of = [&](int buf, int s) -> unsigned char* {
-    const int x = buf * PPB + s;
+  auto vbuf_of = [&](int stage, int s) -> unsigned char* {
+    const int x = stage * PPB + s;
     return x == 0 ? sV0 : x == 1 ? sV1 : x == 2 ? sV2 : sV3;
   };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // uniform by construction; telling the compiler keeps the LDS destinations
-  // of the page copies in scalar registers
+  // of the page copies and the head selection in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hs = wave / NW;                          // head of the workgroup's unit
+  const int wv = wave - hs * NW;                     // wavefront within the head's tile
+  const int tid_h = tid - hs * NTH;                  // thread within the head
+  const bool head_writer = tid_h == 0;
   const int hf = lane >> 5;
   const int col = lane & 31;
 
-  int b, h, i;
-  decode_tile(p, blockIdx.x, b, h, i);
+  int b, hu, i;
+  decode_tile(p, blockIdx.x, p.hq / HP, b, hu, i);
   const int hg = p.hq / p.hkv;
-  const int g = h / hg;
+  const int h = hu * HP + hs;
+  const int g = (hu * HP) / hg;
   const int q0 = p.cu_seqlens[b];
   const int L = p.cu_seqlens[b + 1] - q0;
   const int tile_q0 = i * BQ;
   const int64_t row = ((int64_t)b * p.hq + h) * p.nqb + i;
   if (tile_q0 >= L) {
-    if (kOrdered && p.row_stats != nullptr && tid == 0) {
+    if (kOrdered && p.row_stats != nullptr && head_writer) {
       p.row_stats[2 * row] = 0;
       p.row_stats[2 * row + 1] = 0;
     }
@@ -221,6 +273,8 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
   }
   const int tile_last = min(tile_q0 + BQ, L) - 1;
   // mask row: per query head, or per KV head when the group shares its mask
+  // (the host pairs heads only when they share the mask row, so the slot
+  // count and the page walk are the same for the whole workgroup)
   const int64_t mrow =
       kOrdered ? ((int64_t)b * p.mask_heads + h / (p.hq / p.mask_heads)) * p.nqb + i : row;
   const int cnt = kOrdered ? p.counts[mrow] : tile_last / KVB + 1;
@@ -242,7 +296,7 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
       kOrdered ? p.ordered_pages + mrow * p.capacity * PPB : nullptr;
   const int32_t* __restrict__ pt = p.page_table + (int64_t)b * p.max_pages;
 
-  const int wave_q0 = tile_q0 + wave * 32;
+  const int wave_q0 = tile_q0 + wv * 32;
   const int wave_last = min(wave_q0 + 31, L - 1);
   const int qpos = wave_q0 + col;
   const bool row_valid = qpos < L;
@@ -263,8 +317,8 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
   // Slot -> (logical block, page) lookups come from a two-chunk ring of 64
   // entries in LDS (uniform-address reads, no vector-memory wait on the page
   // loop).  When slot 64c starts, wave 0 copies chunk c+1 from memory straight
-  // into the ring half that chunk c-1 used (HBM -> LDS); it is read 62 slots
-  // and as many barriers later.
+  // into the ring half that chunk c-1 used (HBM -> LDS); it is read at least
+  // 64 - NS slots and as many barriers later.
   // page entries: slot t's pages at page_src[t * PPB + s] (the ordered
   // mask's page list, or the page table, whose logical block t spans pages
   // t * PPB .. t * PPB + PPB - 1)
@@ -306,9 +360,8 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
         __builtin_amdgcn_global_load_lds(
             static_cast<const void*>(ob + t),
             (__attribute__((address_space(3))) void*)&sSlotB[c & 1][0], 4, 0, 0);
-      // once per 64 slots: keeps any ring copy from being outstanding across
-      // the loop back-edge, where the compiler would wait for it (and for the
-      // page prefetches) before every QK
+      // once per 64 slots: the ring copy lands before this wave reaches the
+      // next barrier (and so before any wave reads the chunk)
       __builtin_amdgcn_s_waitcnt(0);
     }
   };
@@ -336,16 +389,27 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
           (__attribute__((address_space(3))) void*)(dst + (e * NT + wave * 64) * 16), 16, 0, 0);
     }
   };
-  // the pages of slot t's logical block j that hold keys of the sequence
-  auto copy_k = [&](int t, int j, int buf) {
+  // the pages of slot t's logical block j that hold keys of the sequence;
+  // returns the number of copy instructions this wavefront issued
+  auto copy_k = [&](int t, int j, int stage) -> int {
+    int n = 0;
 #pragma unroll
     for (int s = 0; s < PPB; ++s)
-      if (s == 0 || j * KVB + s * kPage < L) copy_page(p.k_pool, slot_page(t, s), kbuf(buf, s));
+      if (s == 0 || j * KVB + s * kPage < L) {
+        copy_page(p.k_pool, slot_page(t, s), kbuf(stage, s));
+        n += K_PER;
+      }
+    return n;
   };
-  auto copy_v = [&](int t, int j, int buf) {
+  auto copy_v = [&](int t, int j, int stage) -> int {
+    int n = 0;
 #pragma unroll
     for (int s = 0; s < PPB; ++s)
-      if (s == 0 || j * KVB + s * kPage < L) copy_page(p.v_pool, slot_page(t, s), vbuf_of(buf, s));
+      if (s == 0 || j * KVB + s * kPage < L) {
+        copy_page(p.v_pool, slot_page(t, s), vbuf_of(stage, s));
+        n += K_PER;
+      }
+    return n;
   };
 
   f32x16_t o[DBLK];
@@ -355,6 +419,7 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
   float m_ref = kNegInf;    // reference max of the exponentials (<= m_true)
   float lsum = 0.f;         // this lane's half of the running sum, relative to m_ref
   int nskip = 0;
+  uint32_t rec_word = 0;    // skip bits of the head's current 32 slots
   const bool skip_on = kOrdered && p.skip_mode != kSkipOff;
   // threshold in log2 units: fixed, or log2(L / Delta) for this sequence
   const float tau_l2 = p.skip_mode == kSkipDelta ? __log2f((float)L) - p.log2_delta : p.tau_log2;
@@ -363,19 +428,38 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
   // ---- building blocks of one page step (all straight-line code, so that
   // the compiler can interleave them inside one basic block)
   // S^T(block) = K Q^T for this wave's 32 queries: raw dot products; S^T
-  // block mb holds keys 32mb.. of the logical block (page mb / 2)
-  auto qk = [&](int buf, f32x16_t (&sacc)[MB]) {
+  // block mb holds keys 32mb.. of the logical block (page mb / 2).  The K
+  // operand reads run two k-steps ahead of the products (one with two heads
+  // per workgroup, whose wavefronts hold more state).
+  auto qk = [&](int stage, f32x16_t (&sacc)[MB]) {
+    constexpr int kAhead = HP == 1 ? 2 : 1;
+    u32x4_t a[kAhead + 1][MB];
+    auto load = [&](int ks) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        a[ks % (kAhead + 1)][mb] = *reinterpret_cast<const u32x4_t*>(
+            kbuf(stage, mb >> 1) + PageLayout<D>::offset((mb & 1) * 32 + col, 2 * ks + hf));
+    };
+#pragma unroll
+    for (int ks = 0; ks < kAhead && ks < KSTEPS; ++ks) load(ks);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
+      if (ks + kAhead < KSTEPS) load(ks + kAhead);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-            kbuf(buf, mb >> 1) + PageLayout<D>::offset((mb & 1) * 32 + col, 2 * ks + hf));
+      for (int mb = 0; mb < MB; ++mb)
         sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, a), qf[ks], ks == 0 ? (f32x16_t){} : sacc[mb], 0, 0,
-            0);
-      }
+            __builtin_bit_cast(bf16x8_t, a[ks % (kAhead + 1)][mb]), qf[ks],
+            ks == 0 ? (f32x16_t){} : sacc[mb], 0, 0, 0);
     }
+    // scheduling pattern: the first kAhead + 1 k-steps of reads, then one
+    // k-step of products and one of reads in turn, then the last products
+    __builtin_amdgcn_sched_group_barrier(0x100, (kAhead + 1) * MB, 0);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS - kAhead - 1; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, MB, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, (kAhead + 1) * MB, 0);
   };
   // P = exp2(S * scale_log2 - mu) rounded to bf16 (the P^T operand), row sum
   auto softmax_p = [&](const f32x16_t (&sacc)[MB], float mu, bf16x8_t (&pb)[2 * MB]) -> float {
@@ -403,18 +487,18 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int row = 8 * r + tr_row;
+      const int row_r = 8 * r + tr_row;
 #pragma unroll
       for (int md = 0; md < DBLK; ++md) {
         const int colx = md * 32 + tr_col;
-        vtr[r][md] = PageLayout<D>::offset(row, colx >> 3) + ((colx & 7) << 1);
+        vtr[r][md] = PageLayout<D>::offset(row_r, colx >> 3) + ((colx & 7) << 1);
       }
     }
   }
-  auto pv = [&](int buf, const bf16x8_t (&pb)[2 * MB]) {
+  auto pv = [&](int stage, const bf16x8_t (&pb)[2 * MB]) {
 #pragma unroll
     for (int ks = 0; ks < 4 * PPB; ++ks) {
-      const unsigned char* vb = vbuf_of(buf, ks >> 2);
+      const unsigned char* vb = vbuf_of(stage, ks >> 2);
 #pragma unroll
       for (int md = 0; md < DBLK; ++md) {
         u32x4_t a;
@@ -435,12 +519,12 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
   // Key rows past the end of the sequence in its last block may hold anything
   // (P is 0 there, but 0 * NaN is not; a page past the end was not copied):
   // zero them in the V pages before P V.
-  auto zero_v_tail = [&](int buf, int valid_keys) {
+  auto zero_v_tail = [&](int stage, int valid_keys) {
     constexpr int kRowChunks = D / 8;
 #pragma unroll
     for (int s = 0; s < PPB; ++s) {
       const int valid = min(max(valid_keys - s * kPage, 0), kPage);
-      unsigned char* vb = vbuf_of(buf, s);
+      unsigned char* vb = vbuf_of(stage, s);
       for (int f = valid * kRowChunks + tid; f < kPage * kRowChunks; f += NT)
         *reinterpret_cast<u32x4_t*>(vb + f * 16) = (u32x4_t){0u, 0u, 0u, 0u};
     }
@@ -466,36 +550,47 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
     return pair_max(mx) * c2;
   };
-  auto vote = [&](float bmx, int vbuf) {
+  auto vote = [&](float bmx, int vb) {
     if (skip_on) {
       const bool pred = !row_valid || (bmx < m_true - tau_l2);
       const bool wave_all = __all(pred);
-      if (lane == 0) sVote[vbuf][wave] = wave_all ? 1 : 0;
+      if (lane == 0) sVote[vb][wave] = wave_all ? 1 : 0;
     }
   };
 
-  // Block loop, one workgroup barrier per visited logical block.  Iteration
-  // t: S(t) from the K pages already in LDS, mask, block max and the tile
-  // vote; barrier (every copy issued so far has landed); read the vote; start
-  // the copies of K(t+2) and V(t+1) (HBM -> LDS); then the softmax and P V of
-  // block t unless the tile skips it.
-  int j_cur = 0, j_next = 0;
+  // Block loop, one workgroup barrier per visited logical block.  Step t
+  // (LDS stage t % NS): S(t) from the K pages already in LDS, mask, block max
+  // and the tile vote; wait for this wavefront's copies of V(t) and K(t+1)
+  // (issued NS - 1 steps earlier; the later ones stay in flight), barrier;
+  // read the vote; start the copies of K(t+NS) and V(t+NS-1) into the stages
+  // whose last readers have passed the barrier (HBM -> LDS); then the softmax
+  // and P V of block t unless the head's tile skips it.
+  // With four stages every step issues the same copies (past the last slot
+  // they repeat the last slot's pages into stages no later step reads), so
+  // that the count of copies in flight is the same on every path and the
+  // compiler can tell which ones a wait covers.
   if (cnt > 0) {
-    j_cur = slot_block(0);
-    if (selected(0)) copy_k(0, j_cur, 0);
-    if (cnt > 1) {
-      j_next = slot_block(1);
-      if (selected(1)) copy_k(1, j_next, 1);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int ts = NS == 4 ? min(s, cnt - 1) : s;
+      if ((NS == 4 || s < cnt) && selected(ts)) copy_k(ts, slot_block(ts), s);
     }
-    if (selected(0)) copy_v(0, j_cur, 0);
+#pragma unroll
+    for (int s = 0; s + 1 < NS; ++s) {
+      const int ts = NS == 4 ? min(s, cnt - 1) : s;
+      if ((NS == 4 || s < cnt) && selected(ts)) copy_v(ts, slot_block(ts), s);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  // One step per slot; the slot's LDS buffer (t & 1) is a compile-time
+  // One step per slot; the slot's LDS stage (t % NS) is a compile-time
   // constant, so every LDS operand address is a fixed per-lane offset plus an
   // immediate.
-  auto step = [&](const int t, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
+  auto step = [&](const int t, auto stage_c) {
+    constexpr int st = decltype(stage_c)::value;     // t % NS
+    constexpr int vb = st & 1;                       // vote buffer, t & 1
+    constexpr int st_prev = (st + NS - 1) % NS;      // stage of slot t - 1 and t + NS - 1
+    const int j_cur = slot_block(t);
     const int key0 = j_cur * KVB;
     const bool sel = selected(t);
     // some key of the block is visible to some valid row of this wave
@@ -503,37 +598,50 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
     f32x16_t sacc[MB];
     float bm = kNegInf;
     if (active) {
-      qk(buf, sacc);
+      qk(st, sacc);
       bm = mask_max(j_cur, sacc);
     }
-    vote(bm, buf);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    vote(bm, vb);
+    // V(t) and K(t+1) were issued NS - 1 steps ago; the copies of the NS - 2
+    // steps since then stay in flight
+    wait_vm_c<(NS - 2) * 2 * K_PER * PPB>();
+    lds_barrier();
 
     bool skip = false;
     if (skip_on) {
       int all = 1;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) all &= sVote[buf][w];
-      skip = all != 0;
+      for (int w = 0; w < NW; ++w) all &= sVote[vb][hs * NW + w];
+      skip = __builtin_amdgcn_readfirstlane(all) != 0;   // uniform over the head
     }
     if (kOrdered) {
       nskip += skip ? 1 : 0;
-      if (p.skip_record != nullptr && tid == 0) p.skip_record[row * p.capacity + t] = skip ? 1 : 0;
+      if (p.skip_record != nullptr) {
+        // every lane keeps the (uniform) word; the head writer stores it
+        rec_word |= (skip ? 1u : 0u) << (t & 31);
+        if ((t & 31) == 31 || t + 1 == cnt) {
+          if (head_writer) sRec[hs][t >> 5] = rec_word;
+          rec_word = 0;
+        }
+      }
     }
 
-    // ---- prefetch: K(t+2) and V(t+1) straight into LDS, and the slot chunk
-    // after the one that holds slot t+1
+    // ---- prefetch: K(t+NS) and V(t+NS-1) straight into LDS, and the slot
+    // chunk after the one that holds slot t+1
     advance_chunks(t + 1);
-    const int j_after = j_next;   // block of slot t+1
-    if (t + 2 < cnt) {
-      j_next = slot_block(t + 2);
-      if (selected(t + 2)) copy_k(t + 2, j_next, buf);
+    if constexpr (NS == 4) {
+      const int tk = min(t + NS, cnt - 1);
+      const int tv = min(t + NS - 1, cnt - 1);
+      copy_k(tk, slot_block(tk), st);
+      copy_v(tv, slot_block(tv), st_prev);
+    } else {
+      if (t + NS < cnt && selected(t + NS)) copy_k(t + NS, slot_block(t + NS), st);
+      if (t + NS - 1 < cnt && selected(t + NS - 1))
+        copy_v(t + NS - 1, slot_block(t + NS - 1), st_prev);
     }
-    if (t + 1 < cnt && selected(t + 1)) copy_v(t + 1, j_after, buf ^ 1);
 
-    if (sel && !skip && key0 + KVB > L) {   // uniform: the sequence's last block
-      zero_v_tail(buf, L - key0);
+    if (sel && key0 + KVB > L) {   // uniform: the sequence's last block
+      zero_v_tail(st, L - key0);
       __syncthreads();
     }
     if (active && !skip) {
@@ -552,13 +660,24 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
       const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
       bf16x8_t pb[2 * MB];
       lsum += softmax_p(sacc, mu, pb);
-      pv(buf, pb);
+      pv(st, pb);
     }
-    j_cur = j_after;
   };
-  for (int t = 0; t < cnt; t += 2) {
-    step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < cnt) step(t + 1, std::integral_constant<int, 1>{});
+  // Whole groups of NS steps in the loop, the rest after it: every path
+  // around the loop issues the same copies.
+  int t0 = 0;
+  for (; t0 + NS <= cnt; t0 += NS) {
+    step(t0, std::integral_constant<int, 0>{});
+    step(t0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (NS == 4) {
+      step(t0 + 2, std::integral_constant<int, 2>{});
+      step(t0 + 3, std::integral_constant<int, 3>{});
+    }
+  }
+  if (t0 < cnt) step(t0, std::integral_constant<int, 0>{});
+  if constexpr (NS == 4) {
+    if (t0 + 1 < cnt) step(t0 + 1, std::integral_constant<int, 1>{});
+    if (t0 + 2 < cnt) step(t0 + 2, std::integral_constant<int, 2>{});
   }
 
   // ---- epilogue: out = O / l, lse = m + ln l
@@ -587,37 +706,51 @@ __global__ __launch_bounds__(NW * 64, PPB == 1 ? 2 : 1) void attn_fwd_kernel(con
           ltot > 0.f ? (m_ref + __log2f(ltot)) * kLn2 : kNegInf;
     }
   }
-  if (kOrdered && p.row_stats != nullptr && tid == 0) {
+  if (kOrdered && p.row_stats != nullptr && head_writer) {
     p.row_stats[2 * row] = cnt;
     p.row_stats[2 * row + 1] = nskip;
   }
+  if (kOrdered && p.skip_record != nullptr) {
+    __syncthreads();   // every head writer's last record word is in LDS
+    uint8_t* rec = p.skip_record + row * p.capacity;
+    for (int t = tid_h; t < cnt; t += NTH) rec[t] = (uint8_t)((sRec[hs][t >> 5] >> (t & 31)) & 1u);
+  }
 }
 
-template <int D, int NW, int kMode, int PPB>
+template <int D, int NW, int kMode, int PPB, int HP, int NS>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
-  const int64_t grid = (int64_t)p.batch * p.hq * p.nqb;
+  const int64_t grid = (int64_t)p.batch * (p.hq / HP) * p.nqb;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, kMode, PPB>), dim3((unsigned)grid), dim3(NW * 64),
-                     0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, kMode, PPB, HP, NS>), dim3((unsigned)grid),
+                     dim3(NW * HP * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, int NW>
 hipError_t launch_mode(const AttnParams& p, AttnMode mode, int ppb, hipStream_t stream) {
   if (ppb == 2) {
-    if (mode == kModeOrdered) return launch_one<D, NW, kModeOrdered, 2>(p, stream);
-    if (mode == kModeDense) return launch_one<D, NW, kModeDense, 2>(p, stream);
+    if (mode == kModeOrdered) return launch_one<D, NW, kModeOrdered, 2, 1, 2>(p, stream);
+    if (mode == kModeDense) return launch_one<D, NW, kModeDense, 2, 1, 2>(p, stream);
     return hipErrorInvalidValue;
   }
-  if (mode == kModeOrdered) return launch_one<D, NW, kModeOrdered, 1>(p, stream);
-  if (mode == kModeLogical) return launch_one<D, NW, kModeLogical, 1>(p, stream);
-  return launch_one<D, NW, kModeDense, 1>(p, stream);
+  if (mode == kModeOrdered) return launch_one<D, NW, kModeOrdered, 1, 1, 2>(p, stream);
+  if (mode == kModeLogical) return launch_one<D, NW, kModeLogical, 1, 1, 2>(p, stream);
+  return launch_one<D, NW, kModeDense, 1, 1, 2>(p, stream);
+}
+
+// Two query heads per workgroup for the dense walk (every head of a KV group
+// visits the same pages), four LDS stages.
+hipError_t launch_dense_pairs(const AttnParams& p, hipStream_t stream) {
+  return launch_one<128, 4, kModeDense, 1, 2, 4>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, AttnMode mode,
                             hipStream_t stream) {
+  if (COSA_HEAD_PAIRS && mode == kModeDense && p.ppb == 1 && head_dim == 128 &&
+      q_block == 128 && (p.hq / p.hkv) % 2 == 0)
+    return launch_dense_pairs(p, stream);
   if (head_dim == 128 && q_block == 128) return launch_mode<128, 4>(p, mode, p.ppb, stream);
   if (head_dim == 128 && q_block == 64) return launch_mode<128, 2>(p, mode, p.ppb, stream);
   if (head_dim == 64 && q_block == 128) return launch_mode<64, 4>(p, mode, p.ppb, stream);

@@ -63,6 +63,11 @@ RAGGED = dict(seqlens=(1, 63, 64, 65, 200, 383), num_q_heads=8, num_kv_heads=2,
     ("tiny", dict(RAGGED)),
     ("tiny", dict(RAGGED, q_block=64)),
     ("tiny", dict(RAGGED, head_dim=64, q_block=128)),
+    # query heads per KV group 3 (one head per workgroup), 1 and 2 (two), and
+    # longer sequences: whole groups of four pipeline stages plus remainders
+    ("tiny", dict(RAGGED, num_q_heads=6, num_kv_heads=2)),
+    ("tiny", dict(RAGGED, num_q_heads=4, num_kv_heads=4)),
+    ("tiny", dict(RAGGED, num_q_heads=4, num_kv_heads=2, seqlens=(700, 1031, 129))),
 ])
 def test_dense_matches_oracle(case):
     name, kw = case
