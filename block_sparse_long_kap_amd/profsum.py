@@ -54,7 +54,7 @@ def attention_source_digest(read=None) -> str:
 def entry_of(kernel: str):
     """C entry point that launches an attention kernel instance, from the last
     template argument (the page-walk mode), or None for other kernels."""
-    m = re.search(r"attn_fwd_kernel<\s*\d+,\s*\d+,\s*(\w+)\s*(?:,\s*\d+\s*)?>", kernel)
+    m = re.search(r"attn_fwd_kernel<\s*\d+,\s*\d+,\s*(\w+)\s*(?:,\s*\d+\s*)*>", kernel)
     if not m:
         return None
     return {"0": "cosa_dense_prefill", "false": "cosa_dense_prefill",

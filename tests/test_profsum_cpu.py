@@ -58,4 +58,6 @@ def test_entry_points_from_kernel_names():
     assert profsum.entry_of(k.format(2)) == "cosa_block_mask_prefill"
     assert profsum.entry_of(k.format("1, 2")) == "cosa_osk_prefill"
     assert profsum.entry_of(k.format("0, 1")) == "cosa_dense_prefill"
+    assert profsum.entry_of(k.format("1, 1, 1, 2")) == "cosa_osk_prefill"
+    assert profsum.entry_of(k.format("0, 1, 2, 4")) == "cosa_dense_prefill"
     assert profsum.entry_of("void cosa::(anonymous namespace)::kap_select<128, 8, false>(x)") is None
