@@ -9,4 +9,4 @@ from .api import (KapWorkspace, OrderedMask, PrefillOutput, Problem,  # noqa: F4
                   block_mask_prefill, dense_prefill, osk_prefill, osk_prefill_delta,
                   osk_prefill_shared_kv,
                   proxy_ordered_mask, proxy_ordered_mask_shared_kv, proxy_ordered_mask_top_p,
-                  tau_from_delta)
+                  sparse_prefill, tau_from_delta)

@@ -68,6 +68,8 @@ SIGNATURES = {
     "cosa_osk_prefill_delta": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_f32, c_vp,
                                        c_vp, c_vp, c_vp, c_vp]),
     "cosa_dense_prefill": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "cosa_sparse_prefill": (c_i32, [P, c_vp, c_vp, c_vp, c_f32, c_f32, c_vp, c_vp, c_vp, c_vp,
+                                    c_i64, c_vp, c_size, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "cosa_block_mask_prefill": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp]),
 }
 

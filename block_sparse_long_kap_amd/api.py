@@ -301,6 +301,29 @@ def osk_prefill_delta(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor,
     return out
 
 
+def sparse_prefill(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                   budget: float, skip_tau: float, *, aux_stream: Optional[torch.cuda.Stream] = None,
+                   capacity: Optional[int] = None, hrm_counts: bool = True,
+                   workspace: Optional[KapWorkspace] = None, mask: Optional[OrderedMask] = None,
+                   lse: bool = True, record: bool = True,
+                   out: Optional[PrefillOutput] = None):
+    """KAP mask and OSK attention in one call (``cosa_sparse_prefill``); returns
+    (mask, output).  With ``aux_stream`` the kernel of each chunk of KV groups
+    runs there while the proxy of the next chunk runs on the current stream."""
+    lib = _lib.load()
+    mask = _mask_buffers(problem, q, k_pool, budget, capacity, hrm_counts, False, mask)
+    ws = workspace if workspace is not None else KapWorkspace(problem)
+    out = _prefill_buffers(problem, q, k_pool, v_pool, mask, lse, record, out)
+    aux = None if aux_stream is None else ctypes.c_void_p(aux_stream.cuda_stream)
+    st = lib.cosa_sparse_prefill(
+        problem.ref(), _ptr(q), _ptr(k_pool), _ptr(v_pool), ctypes.c_float(budget),
+        ctypes.c_float(skip_tau), _ptr(mask.blocks), _ptr(mask.pages), _ptr(mask.counts),
+        _ptr(mask.hrm_counts), mask.capacity, _ptr(ws.buf), ws.nbytes, _ptr(out.out),
+        _ptr(out.lse), _ptr(out.skip_record), _ptr(out.row_stats), _stream(problem.device), aux)
+    _lib.check(st, "cosa_sparse_prefill")
+    return mask, out
+
+
 def dense_prefill(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                   *, lse: bool = True, out: Optional[PrefillOutput] = None) -> PrefillOutput:
     """Dense causal prefill on the same kernel (``cosa_dense_prefill``)."""

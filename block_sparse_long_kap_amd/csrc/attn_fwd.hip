@@ -142,8 +142,9 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, int bid, int hq
     // working set is that group's pages (64 MB at 128K) and repeated page
     // visits across tiles and query heads hit the memory-side cache
     const int per_group = hg * p.nqb;
-    const int G = bid / per_group;
-    const int r = bid - G * per_group;
+    const int local = bid / per_group;
+    const int G = p.group_begin + local;
+    const int r = bid - local * per_group;
     const int level = r / hg;
     const int hh = r - level * hg;
     b = G / p.hkv;
@@ -719,7 +720,8 @@ __global__ __launch_bounds__(NW * HP * 64, (PPB == 1 && HP == 1) ? 2 : 1) void a
 
 template <int D, int NW, int kMode, int PPB, int HP, int NS>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
-  const int64_t grid = (int64_t)p.batch * (p.hq / HP) * p.nqb;
+  const int64_t n_groups = p.group_count > 0 ? p.group_count : (int64_t)p.batch * p.hkv;
+  const int64_t grid = n_groups * (p.hq / p.hkv / HP) * p.nqb;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL((attn_fwd_kernel<D, NW, kMode, PPB, HP, NS>), dim3((unsigned)grid),
                      dim3(NW * HP * 64), 0, stream, p);
@@ -748,6 +750,8 @@ hipError_t launch_dense_pairs(const AttnParams& p, hipStream_t stream) {
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, AttnMode mode,
                             hipStream_t stream) {
+  // a range of groups is only defined in the group-major order
+  if (p.group_count > 0 && p.order != kOrderGroupMajor) return hipErrorInvalidValue;
   if (COSA_HEAD_PAIRS && mode == kModeDense && p.ppb == 1 && head_dim == 128 &&
       q_block == 128 && (p.hq / p.hkv) % 2 == 0)
     return launch_dense_pairs(p, stream);

@@ -115,6 +115,8 @@ void fill_attn(cosa::AttnParams& a, const cosa_problem* p, const void* q, const 
 #define COSA_TILE_ORDER cosa::kOrderGroupMajor
 #endif
   a.order = COSA_TILE_ORDER;
+  a.group_begin = 0;
+  a.group_count = 0;
   if (a.order == cosa::kOrderXcdGroup && a.xcd_groups == 0) a.order = cosa::kOrderLevel;
   if (a.order == cosa::kOrderGroupXcd && a.xcd_units == 0) a.order = cosa::kOrderGroupMajor;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
@@ -189,10 +191,12 @@ COSA_EXPORT cosa_status cosa_check_page_table_host(const cosa_problem* p,
 
 namespace {
 
-cosa_status proxy_mask(const cosa_problem* p, const void* q, const void* k_pool, float budget,
-                       uint64_t top_p_fx, bool shared, int32_t* ordered_blocks, int32_t* ordered_pages,
-                       int32_t* counts, int32_t* hrm_counts, float* debug_w, uint8_t* debug_hrm,
-                       int64_t capacity, void* workspace, size_t workspace_bytes, void* stream) {
+// Validates the proxy's arguments and fills its kernel parameters.
+cosa_status build_kap(cosa::KapParams& k, const cosa_problem* p, const void* q, const void* k_pool,
+                      float budget, uint64_t top_p_fx, bool shared, int32_t* ordered_blocks,
+                      int32_t* ordered_pages, int32_t* counts, int32_t* hrm_counts, float* debug_w,
+                      uint8_t* debug_hrm, int64_t capacity, void* workspace,
+                      size_t workspace_bytes) {
   cosa_status st = validate(p);
   if (st != COSA_OK) return st;
   if (q == nullptr || k_pool == nullptr || ordered_blocks == nullptr ||
@@ -208,7 +212,6 @@ cosa_status proxy_mask(const cosa_problem* p, const void* q, const void* k_pool,
   const size_t need = cosa_kap_workspace_size(p);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(COSA_ERR_WORKSPACE, "workspace null or smaller than cosa_kap_workspace_size()");
-  cosa::KapParams k;
   k.q = static_cast<const uint16_t*>(q);
   k.k_pool = static_cast<const uint16_t*>(k_pool);
   k.cu_seqlens = p->cu_seqlens;
@@ -232,6 +235,8 @@ cosa_status proxy_mask(const cosa_problem* p, const void* q, const void* k_pool,
   k.beta_ppm = ppm;
   k.scale = p->softmax_scale;
   k.top_p_fx = top_p_fx;
+  k.group_begin = 0;
+  k.group_count = 0;
   k.shared_heads = 0;
   if (shared) {
     const int hg = p->num_q_heads / p->num_kv_heads;
@@ -243,6 +248,18 @@ cosa_status proxy_mask(const cosa_problem* p, const void* q, const void* k_pool,
       k.shared_heads = hg;
     }
   }
+  return COSA_OK;
+}
+
+cosa_status proxy_mask(const cosa_problem* p, const void* q, const void* k_pool, float budget,
+                       uint64_t top_p_fx, bool shared, int32_t* ordered_blocks, int32_t* ordered_pages,
+                       int32_t* counts, int32_t* hrm_counts, float* debug_w, uint8_t* debug_hrm,
+                       int64_t capacity, void* workspace, size_t workspace_bytes, void* stream) {
+  cosa::KapParams k;
+  const cosa_status st =
+      build_kap(k, p, q, k_pool, budget, top_p_fx, shared, ordered_blocks, ordered_pages, counts,
+                hrm_counts, debug_w, debug_hrm, capacity, workspace, workspace_bytes);
+  if (st != COSA_OK) return st;
   return hip_status(cosa::launch_kap(k, p->head_dim, p->q_block, (hipStream_t)stream));
 }
 
@@ -310,6 +327,79 @@ COSA_EXPORT cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, c
   }
   return hip_status(
       cosa::launch_attention(a, p->head_dim, p->q_block, cosa::kModeOrdered, (hipStream_t)stream));
+}
+
+COSA_EXPORT cosa_status cosa_sparse_prefill(
+    const cosa_problem* p, const void* q, const void* k_pool, const void* v_pool, float budget,
+    float skip_tau, int32_t* ordered_blocks, int32_t* ordered_pages, int32_t* counts,
+    int32_t* hrm_counts, int64_t capacity, void* workspace, size_t workspace_bytes, void* out,
+    float* lse, uint8_t* skip_record, int32_t* row_stats, void* stream, void* aux_stream) {
+  cosa::KapParams k;
+  cosa_status st = build_kap(k, p, q, k_pool, budget, 0, false, ordered_blocks, ordered_pages,
+                             counts, hrm_counts, nullptr, nullptr, capacity, workspace,
+                             workspace_bytes);
+  if (st != COSA_OK) return st;
+  if (v_pool == nullptr || out == nullptr)
+    return fail(COSA_ERR_INVALID_ARG, "v_pool and out are required");
+  if (isnan(skip_tau)) return fail(COSA_ERR_INVALID_ARG, "skip_tau is NaN");
+  if (aux_stream != nullptr && aux_stream == stream)
+    return fail(COSA_ERR_INVALID_ARG, "aux_stream must differ from stream");
+  cosa::AttnParams a;
+  fill_attn(a, p, q, k_pool, v_pool, out, lse);
+  a.ordered_blocks = ordered_blocks;
+  a.ordered_pages = ordered_pages;
+  a.counts = counts;
+  a.skip_record = skip_record;
+  a.row_stats = row_stats;
+  a.capacity = capacity;
+  a.order = cosa::kOrderGroupMajor;   // group ranges are defined in this order
+  if (skip_tau >= 0.f) {
+    a.skip_mode = cosa::kSkipTau;
+    a.tau_log2 = skip_tau * 1.4426950408889634f;
+  }
+  const hipStream_t s0 = (hipStream_t)stream;
+  const hipStream_t s1 = (hipStream_t)aux_stream;
+  hipError_t e = cosa::launch_kap(k, p->head_dim, p->q_block, s0, cosa::kKapPool);
+  if (e != hipSuccess) return hip_status(e);
+  // (sequence, KV head) groups in at most 8 chunks: the proxy of chunk c+1
+  // runs while the kernel of chunk c does
+  const int n_groups = p->batch * p->num_kv_heads;
+  const int chunk = (n_groups + 7) / 8;
+  hipEvent_t ev[9] = {};
+  int n_ev = 0;
+  auto cleanup = [&]() {
+    for (int x = 0; x < n_ev; ++x) (void)hipEventDestroy(ev[x]);
+  };
+  for (int g0 = 0; g0 < n_groups; g0 += chunk) {
+    const int cnt = n_groups - g0 < chunk ? n_groups - g0 : chunk;
+    k.group_begin = a.group_begin = g0;
+    k.group_count = a.group_count = cnt;
+    e = cosa::launch_kap(k, p->head_dim, p->q_block, s0, cosa::kKapSelect);
+    if (e != hipSuccess) break;
+    hipStream_t s_attn = s0;
+    if (s1 != nullptr) {
+      e = hipEventCreateWithFlags(&ev[n_ev], hipEventDisableTiming);
+      if (e != hipSuccess) break;
+      ++n_ev;
+      e = hipEventRecord(ev[n_ev - 1], s0);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s1, ev[n_ev - 1], 0);
+      if (e != hipSuccess) break;
+      s_attn = s1;
+    }
+    e = cosa::launch_attention(a, p->head_dim, p->q_block, cosa::kModeOrdered, s_attn);
+    if (e != hipSuccess) break;
+  }
+  if (e == hipSuccess && s1 != nullptr) {
+    // the caller's stream continues after the last chunk's kernel
+    e = hipEventCreateWithFlags(&ev[n_ev], hipEventDisableTiming);
+    if (e == hipSuccess) {
+      ++n_ev;
+      e = hipEventRecord(ev[n_ev - 1], s1);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s0, ev[n_ev - 1], 0);
+    }
+  }
+  cleanup();
+  return hip_status(e);
 }
 
 COSA_EXPORT cosa_status cosa_osk_prefill_shared_kv(

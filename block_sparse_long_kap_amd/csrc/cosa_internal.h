@@ -44,6 +44,9 @@ struct AttnParams {
   int32_t xcd_groups;             // B*Hkv when it is a multiple of 8, else 0
   int32_t xcd_units;              // B*Hkv*NQB when it is a multiple of 8, else 0
   int32_t order;                  // tile order, one of TileOrder
+  // (sequence, KV head) groups [group_begin, group_begin + group_count) only
+  // (group_count 0: every group); needs the group-major order
+  int32_t group_begin, group_count;
   float scale_log2;               // softmax_scale * log2(e)
   int32_t skip_mode;              // OSK: kSkipOff, kSkipTau or kSkipDelta
   float tau_log2;                 // kSkipTau: threshold * log2(e)
@@ -90,10 +93,17 @@ struct KapParams {
   // 0: one mask per query head; else the number of query heads per KV head,
   // one mask per KV head shared by them
   int32_t shared_heads;
+  // (sequence, KV head) groups [group_begin, group_begin + group_count) only
+  // (group_count 0: every group)
+  int32_t group_begin, group_count;
 };
+
+// Parts of the proxy to launch.
+enum KapStage : int32_t { kKapPool = 1, kKapSelect = 2, kKapAll = 3 };
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, AttnMode mode,
                             hipStream_t stream);
-hipError_t launch_kap(const KapParams& p, int head_dim, int q_block, hipStream_t stream);
+hipError_t launch_kap(const KapParams& p, int head_dim, int q_block, hipStream_t stream,
+                      KapStage stage = kKapAll);
 
 }  // namespace cosa

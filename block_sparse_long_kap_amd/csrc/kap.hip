@@ -178,8 +178,9 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   const int ngroups = (p.nqb + TPW - 1) / TPW;
   const int hg = p.hq / p.hkv;
   const int per_kv = kShared ? ngroups : ngroups * hg;
-  const int G = blockIdx.x / per_kv;
-  const int rem = blockIdx.x - G * per_kv;
+  const int local = blockIdx.x / per_kv;
+  const int G = p.group_begin + local;
+  const int rem = blockIdx.x - local * per_kv;
   const int level = kShared ? rem : rem / hg;
   const int b = G / p.hkv;
   const int g = G - b * p.hkv;
@@ -685,15 +686,20 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
 }
 
 template <int D, int R>
-hipError_t launch_kap_t(const KapParams& p, hipStream_t stream) {
+hipError_t launch_kap_t(const KapParams& p, hipStream_t stream, KapStage stage) {
   const bool top_p = p.top_p_fx != 0;
   const int nkb = p.n_max;
   if (p.batch <= 0 || nkb <= 0) return hipSuccess;
-  hipLaunchKernelGGL((kap_pool_keys<D>), dim3(nkb, p.batch), dim3(256), 0, stream, p);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (stage & kKapPool) {
+    hipLaunchKernelGGL((kap_pool_keys<D>), dim3(nkb, p.batch), dim3(256), 0, stream, p);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (!(stage & kKapSelect)) return hipSuccess;
+  // workgroups per (sequence, KV head) group, times the groups launched
+  const int64_t n_groups = p.group_count > 0 ? p.group_count : (int64_t)p.batch * p.hkv;
   if (p.shared_heads > 1) {
-    const int64_t grid = (int64_t)p.batch * p.hkv * p.nqb;
+    const int64_t grid = n_groups * p.nqb;
 #define COSA_KAP_SHARED(HPW_)                                                                \
   if constexpr (HPW_ * R <= 32) {                                                          \
     if (p.shared_heads == HPW_) {                                                          \
@@ -713,7 +719,7 @@ hipError_t launch_kap_t(const KapParams& p, hipStream_t stream) {
     return hipErrorInvalidValue;
   }
   const int64_t groups = (p.nqb + kTilesPerGroup - 1) / kTilesPerGroup;
-  const int64_t grid = (int64_t)p.batch * p.hq * groups;
+  const int64_t grid = n_groups * (p.hq / p.hkv) * groups;
   if (top_p)
     hipLaunchKernelGGL((kap_select<D, R, true, 1>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   else
@@ -723,11 +729,12 @@ hipError_t launch_kap_t(const KapParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_kap(const KapParams& p, int head_dim, int q_block, hipStream_t stream) {
-  if (head_dim == 128 && q_block == 128) return launch_kap_t<128, 8>(p, stream);
-  if (head_dim == 128 && q_block == 64) return launch_kap_t<128, 4>(p, stream);
-  if (head_dim == 64 && q_block == 128) return launch_kap_t<64, 8>(p, stream);
-  if (head_dim == 64 && q_block == 64) return launch_kap_t<64, 4>(p, stream);
+hipError_t launch_kap(const KapParams& p, int head_dim, int q_block, hipStream_t stream,
+                      KapStage stage) {
+  if (head_dim == 128 && q_block == 128) return launch_kap_t<128, 8>(p, stream, stage);
+  if (head_dim == 128 && q_block == 64) return launch_kap_t<128, 4>(p, stream, stage);
+  if (head_dim == 64 && q_block == 128) return launch_kap_t<64, 8>(p, stream, stage);
+  if (head_dim == 64 && q_block == 64) return launch_kap_t<64, 4>(p, stream, stage);
   return hipErrorInvalidValue;
 }
 

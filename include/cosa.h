@@ -239,6 +239,32 @@ cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, const void* k
                              uint8_t* skip_record, int32_t* row_stats, void* stream);
 
 /*
+ * The proxy and the Ordered-Skipping Kernel in one call (CoSA (paperpeel)
+ * §4.1: KAP emits the ordered mask that the OSK consumes).  Same result, bit
+ * for bit, as cosa_proxy_ordered_mask() followed by cosa_osk_prefill() with
+ * these arguments (debug_w and debug_hrm not available): the masks are
+ * written to ordered_blocks / ordered_pages / counts / hrm_counts and the
+ * attention to out / lse / skip_record / row_stats, with the layouts given
+ * there.
+ *
+ * The work is cut into at most 8 chunks of (sequence, KV head) groups; the
+ * proxy of every chunk runs on `stream`.  With aux_stream != NULL (another
+ * stream of the same device, not `stream`), the kernel of chunk c runs on
+ * aux_stream after the proxy of chunk c, so that the proxy of later chunks
+ * overlaps it, and `stream` waits for the last kernel before the call's
+ * later work; with aux_stream == NULL everything runs on `stream` in chunk
+ * order.  Argument errors as for the two calls; COSA_ERR_HIP if an event
+ * cannot be created.  The call allocates no device memory.
+ */
+cosa_status cosa_sparse_prefill(const cosa_problem* p, const void* q, const void* k_pool,
+                                const void* v_pool, float budget, float skip_tau,
+                                int32_t* ordered_blocks, int32_t* ordered_pages, int32_t* counts,
+                                int32_t* hrm_counts, int64_t capacity, void* workspace,
+                                size_t workspace_bytes, void* out, float* lse,
+                                uint8_t* skip_record, int32_t* row_stats, void* stream,
+                                void* aux_stream);
+
+/*
  * Ordered-Skipping Kernel over masks shared per KV head (the layout of
  * cosa_proxy_ordered_mask_shared_kv()): query head h of sequence b, tile i
  * walks mask row (b, h / (num_q_heads / num_kv_heads), i).  Everything else,

@@ -147,6 +147,17 @@ def test_entry_points_reject_bad_buffers(lib):
                                           None) == E
     assert lib.cosa_osk_prefill_delta(pr, 1, 1, 1, None, 1, 1, 5, 200.0, 1, None, None, None,
                                       None) == E
+    # the fused call checks both halves' arguments before any launch
+    def fused(budget=0.1, tau=8.0, v=1, capacity=cap, wsb=ws, out=1, stream=None, aux=None):
+        return lib.cosa_sparse_prefill(pr, 1, 1, v, budget, tau, 1, 1, 1, None, capacity, 1, wsb,
+                                       out, None, None, None, stream, aux)
+    assert fused(budget=0.0) == E
+    assert fused(capacity=cap - 1) == E
+    assert fused(wsb=ws - 1) == _lib.COSA_ERR_WORKSPACE
+    assert fused(v=None) == E
+    assert fused(out=None) == E
+    assert fused(tau=float("nan")) == E
+    assert fused(stream=7, aux=7) == E
     # the proxy handles at most 2048 key blocks per sequence
     big = _problem(max_seqlen=131073, max_pages_per_seq=2049, total_q=131073)
     assert lib.cosa_proxy_ordered_mask(ctypes.byref(big), 1, 1, 0.1, 1, 1, 1, None, None, None,

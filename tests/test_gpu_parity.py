@@ -565,3 +565,44 @@ def test_empty_sequences_and_single_block_budget():
                                  w.q_block, w.block, 0.5, w.softmax_scale, shared_kv=True)
     _run_osk_vs_oracle(w, x, ms.blocks, ms.counts, 4.0, "osk shared, empty sequences",
                        shared=True)
+
+
+@pytest.mark.parametrize("case", [
+    ("tiny_skip", {}, 0.5, 2.0),
+    # 6 sequences x 2 KV heads = 12 groups: chunks of 2 groups, the last ones empty
+    ("tiny", dict(RAGGED, q_dir_gain=6.0), 0.2, 2.0),
+    ("tiny", dict(RAGGED, seqlens=(1500, 0, 700, 2047), num_kv_heads=4), 0.3, -1.0),
+])
+@pytest.mark.parametrize("aux", [False, True])
+def test_fused_proxy_and_kernel_equal_separate_calls(case, aux):
+    """cosa_sparse_prefill gives, bit for bit, what cosa_proxy_ordered_mask followed by
+    cosa_osk_prefill give, on one stream and with the kernel on a second stream."""
+    name, kw, budget, tau = case
+    w, x = _inputs(name, **kw)
+    print(f"[case] fused {name} {kw} budget={budget} tau={tau} aux={aux}", flush=True)
+    prob, q, k, v = upload(x, DEV)
+    m1 = bk.proxy_ordered_mask(prob, q, k, budget)
+    r1 = bk.osk_prefill(prob, q, k, v, m1, tau, record=True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(DEV) if aux else None
+    # poison the outputs so that anything the fused call fails to write shows
+    m2 = bk.proxy_ordered_mask(prob, q, k, budget)
+    r2 = bk.osk_prefill(prob, q, k, v, m2, tau, record=True)
+    for t in (m2.blocks, m2.pages, m2.counts, m2.hrm_counts, r2.row_stats):
+        t.fill_(-7)
+    r2.out.fill_(float("nan"))
+    r2.lse.fill_(float("nan"))
+    r2.skip_record.fill_(9)
+    m2, r2 = bk.sparse_prefill(prob, q, k, v, budget, tau, aux_stream=side, mask=m2, out=r2)
+    torch.cuda.synchronize()
+    for a, b_ in ((m1.blocks, m2.blocks), (m1.pages, m2.pages), (m1.counts, m2.counts),
+                  (m1.hrm_counts, m2.hrm_counts), (r1.row_stats, r2.row_stats)):
+        assert torch.equal(a, b_)
+    assert torch.equal(r1.out.view(torch.int16), r2.out.view(torch.int16))
+    assert torch.equal(r1.lse.view(torch.int32), r2.lse.view(torch.int32))
+    # the skip record: equal on every slot below the count (the rest is untouched)
+    cnt = m1.counts.reshape(-1).cpu().numpy()
+    s1 = r1.skip_record.reshape(cnt.size, -1).cpu().numpy()
+    s2 = r2.skip_record.reshape(cnt.size, -1).cpu().numpy()
+    for row, c in enumerate(cnt):
+        assert np.array_equal(s1[row, :c], s2[row, :c])
