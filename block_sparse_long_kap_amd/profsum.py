@@ -3,6 +3,7 @@
 Usage (after the rocprofv3 runs named in each mode's docstring)::
 
     python -m block_sparse_long_kap_amd.profsum stats    KERNEL_STATS.csv  --command "..."
+    python -m block_sparse_long_kap_amd.profsum trace    KERNEL_TRACE.csv  --command "..."
     python -m block_sparse_long_kap_amd.profsum traffic  FETCH.csv WRITE.csv COPY_FETCH.csv \
         COPY_WRITE.csv --copy-bytes 1073741824 --workload llama128k --budget 0.1 --tau 8 \
         --command "..."
@@ -91,6 +92,23 @@ def stats_md(path, command):
     return "\n".join([f"Command: `{command}`", "", *out])
 
 
+def trace_md(path, command):
+    """Per-dispatch kernel times grouped by (kernel, grid size): launches of
+    one kernel over different parts of the work are kept apart."""
+    agg = collections.defaultdict(list)
+    for r in _rows(path):
+        key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) *
+               int(r["Grid_Size_Z"]) // max(1, int(r["Workgroup_Size_X"]) *
+                                            int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])))
+        agg[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+    out = ["| kernel | workgroups | calls | avg ms | min ms | max ms | total ms |",
+           "|---|---|---|---|---|---|---|"]
+    for (k, wg), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| `{k}` | {wg} | {len(v)} | {sum(v) / len(v):.4f} | {min(v):.4f} | "
+                   f"{max(v):.4f} | {sum(v):.3f} |")
+    return "\n".join([f"Command: `{command}`", "", *out])
+
+
 def _copy_kib(path, counter):
     """Largest per-dispatch value of ``counter`` for the device copy kernel."""
     best = 0.0
@@ -176,6 +194,9 @@ def main(argv=None):
     s = sub.add_parser("stats")
     s.add_argument("csv")
     s.add_argument("--command", required=True)
+    tr = sub.add_parser("trace")
+    tr.add_argument("csv")
+    tr.add_argument("--command", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("fetch")
     t.add_argument("write")
@@ -192,6 +213,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.mode == "stats":
         print(stats_md(a.csv, a.command))
+    elif a.mode == "trace":
+        print(trace_md(a.csv, a.command))
     elif a.mode == "traffic":
         print(traffic_md(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes, a.workload,
                          a.budget, a.tau, a.command))

@@ -61,3 +61,19 @@ def test_entry_points_from_kernel_names():
     assert profsum.entry_of(k.format("1, 1, 1, 2")) == "cosa_osk_prefill"
     assert profsum.entry_of(k.format("0, 1, 2, 4")) == "cosa_dense_prefill"
     assert profsum.entry_of("void cosa::(anonymous namespace)::kap_select<128, 8, false>(x)") is None
+
+
+def test_trace_groups_launches_by_grid(tmp_path):
+    hdr = ('"Kind","Kernel_Name","Start_Timestamp","End_Timestamp","Workgroup_Size_X",'
+           '"Workgroup_Size_Y","Workgroup_Size_Z","Grid_Size_X","Grid_Size_Y","Grid_Size_Z"\n')
+    k = "void cosa::(anonymous namespace)::attn_fwd_kernel<128, 4, 1, 1, 1, 2>(cosa::AttnParams)"
+    rows = [(k, 0, 2_000_000, 256, 8192), (k, 0, 4_000_000, 256, 8192),
+            (k, 0, 500_000, 256, 1024)]
+    p = tmp_path / "trace.csv"
+    p.write_text(hdr + "".join(f'"KERNEL_DISPATCH","{n}",{a},{b},{w},1,1,{g},1,1\n'
+                               for n, a, b, w, g in rows))
+    md = profsum.trace_md(str(p), "cmd")
+    lines = [l for l in md.splitlines() if l.startswith("| `attn")]
+    assert len(lines) == 2
+    assert "| 32 | 2 | 3.0000 | 2.0000 | 4.0000 | 6.000 |" in lines[0]
+    assert "| 4 | 1 | 0.5000 |" in lines[1]
