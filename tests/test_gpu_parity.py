@@ -572,6 +572,8 @@ def test_empty_sequences_and_single_block_budget():
     # 6 sequences x 2 KV heads = 12 groups: chunks of 2 groups, the last ones empty
     ("tiny", dict(RAGGED, q_dir_gain=6.0), 0.2, 2.0),
     ("tiny", dict(RAGGED, seqlens=(1500, 0, 700, 2047), num_kv_heads=4), 0.3, -1.0),
+    # 128-key logical blocks over two pages
+    ("tiny_skip", dict(kv_block=128), 0.5, 2.0),
 ])
 @pytest.mark.parametrize("aux", [False, True])
 def test_fused_proxy_and_kernel_equal_separate_calls(case, aux):
