@@ -161,8 +161,10 @@ COSA_EXPORT int64_t cosa_mask_capacity(const cosa_problem* p, float budget) {
 COSA_EXPORT size_t cosa_kap_workspace_size(const cosa_problem* p) {
   if (validate(p) != COSA_OK) return 0;
   const int64_t n_max = ceil_div(p->max_seqlen, p->kv_block);
-  // pooled keys as a bf16 hi plane and a bf16 lo plane
-  return (size_t)2 * p->batch * p->num_kv_heads * p->head_dim * n_max * sizeof(uint16_t);
+  // pooled keys as a bf16 hi plane and a bf16 lo plane, blocks padded to a
+  // multiple of 32
+  const int64_t n_pad = ceil_div(n_max, 32) * 32;
+  return (size_t)2 * p->batch * p->num_kv_heads * p->head_dim * n_pad * sizeof(uint16_t);
 }
 
 COSA_EXPORT cosa_status cosa_check_page_table_host(const cosa_problem* p,

@@ -74,7 +74,10 @@ struct KapParams {
   const uint16_t* k_pool;
   const int32_t* cu_seqlens;
   const int32_t* page_table;
-  uint16_t* kbar;                 // workspace bf16 [hi|lo][B][Hkv][n_max][D]
+  // workspace: pooled keys, bf16 hi and lo planes, each [B][Hkv] of
+  // ceil(n_max / 32) candidate groups laid out as the score product reads
+  // them: [group][D / 16][2][32 blocks][8]
+  uint16_t* kbar;
   int32_t* ordered_blocks;
   int32_t* ordered_pages;
   int32_t* counts;

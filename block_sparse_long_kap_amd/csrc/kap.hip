@@ -56,8 +56,20 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
 }
 
 // ---------------------------------------------------------------------------
-// Key pooling: kbar[plane][b][g][j][d] = mean of the valid keys of block j,
-// plane 0 = bf16 hi, plane 1 = bf16 lo.
+// Key pooling: the mean of the valid keys of block j, plane 0 = bf16 hi,
+// plane 1 = bf16 lo, stored for the score product's operand reads: element d
+// of block j at [(j / 32)][d / 16][(d / 8) % 2][j % 32][d % 8] of its
+// (plane, sequence, KV head) slab, so that one k-step of 32 blocks is 1 KB of
+// consecutive bytes (one coalesced 16-byte read per lane).
+template <int D>
+__device__ __forceinline__ int64_t kbar_offset(int j, int d) {
+  return ((((int64_t)(j >> 5) * (D / 16) + (d >> 4)) * 2 + ((d >> 3) & 1)) * 32 + (j & 31)) * 8 +
+         (d & 7);
+}
+// elements of one (plane, sequence, KV head) slab
+__device__ __forceinline__ int64_t kbar_slab(int n_max, int D) {
+  return (int64_t)((n_max + 31) / 32) * 32 * D;
+}
 template <int D>
 __global__ __launch_bounds__(256) void kap_pool_keys(const KapParams p) {
   constexpr int NT = 256;
@@ -76,7 +88,8 @@ __global__ __launch_bounds__(256) void kap_pool_keys(const KapParams p) {
   const int c = tid % KCH;
   const int rg = tid / KCH;
   const float inv = 1.f / (float)nvalid;
-  const int64_t plane = (int64_t)p.batch * p.hkv * p.n_max * D;
+  const int64_t slab = kbar_slab(p.n_max, D);
+  const int64_t plane = (int64_t)p.batch * p.hkv * slab;
 
   for (int g = 0; g < p.hkv; ++g) {
     float acc[8];
@@ -101,7 +114,7 @@ __global__ __launch_bounds__(256) void kap_pool_keys(const KapParams p) {
       for (int k = 0; k < RG; ++k) sum += red[k][tid];
       uint16_t hi, lo;
       split_bf16(sum * inv, hi, lo);
-      const int64_t at = (((int64_t)b * p.hkv + g) * p.n_max + j) * D + tid;
+      const int64_t at = ((int64_t)b * p.hkv + g) * slab + kbar_offset<D>(j, tid);
       p.kbar[at] = hi;
       p.kbar[plane + at] = lo;
     }
@@ -192,7 +205,6 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   const int q0 = p.cu_seqlens[b];
   const int L = p.cu_seqlens[b + 1] - q0;
   const int kvb = p.kv_block;
-  const int nkb = (L + kvb - 1) / kvb;
   const int32_t* __restrict__ pt = p.page_table + (int64_t)b * p.max_pages;
 
   // per-tile sizes (n = 0 for a tile past the sequence's end)
@@ -302,8 +314,9 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) cand[r] = row_cand(8 * (r >> 2) + 4 * hf + (r & 3));
 
-  const int64_t plane = (int64_t)p.batch * p.hkv * p.n_max * D;
-  const uint16_t* kb_hi = p.kbar + ((int64_t)b * p.hkv + g) * p.n_max * D;
+  const int64_t slab = kbar_slab(p.n_max, D);
+  const int64_t plane = (int64_t)p.batch * p.hkv * slab;
+  const uint16_t* kb_hi = p.kbar + ((int64_t)b * p.hkv + g) * slab;
   const uint16_t* kb_lo = kb_hi + plane;
   const int nb = (n_wg + 31) / 32;
 
@@ -311,14 +324,14 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   // wave loads its next block right after the current block's products, so
   // the loads travel while the row statistics are updated
   bf16x8_t kh[KSTEPS], kl[KSTEPS];
+  // (blocks past the sequence's last one hold stale values; their scores
+  // are masked)
   auto load_ops = [&](int cb) {
-    const int j = min(cb * 32 + col, nkb - 1);   // clamp reads; masked later
-    const uint16_t* bh = kb_hi + (int64_t)j * D + hf * 8;
-    const uint16_t* bl = kb_lo + (int64_t)j * D + hf * 8;
+    const int64_t at = kbar_offset<D>(cb * 32 + col, hf * 8);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      kh[ks] = *reinterpret_cast<const bf16x8_t*>(bh + ks * 16);
-      kl[ks] = *reinterpret_cast<const bf16x8_t*>(bl + ks * 16);
+      kh[ks] = *reinterpret_cast<const bf16x8_t*>(kb_hi + at + ks * (2 * 32 * 8));
+      kl[ks] = *reinterpret_cast<const bf16x8_t*>(kb_lo + at + ks * (2 * 32 * 8));
     }
   };
   // scores of the loaded block for the 32 rows (log2 units)

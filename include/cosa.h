@@ -104,9 +104,9 @@ int64_t cosa_num_q_tiles(const cosa_problem* p);
 int64_t cosa_mask_capacity(const cosa_problem* p, float budget);
 
 /* Bytes of device workspace cosa_proxy_ordered_mask() needs: the pooled keys
- * as two bf16 planes (hi, lo) of [batch][num_kv_heads][n_max][head_dim],
- * i.e. 4 bytes per (sequence, KV head, key block, dim).  0 on an invalid
- * problem. */
+ * as two bf16 planes (hi, lo) of [batch][num_kv_heads][n_pad][head_dim] with
+ * n_pad = n_max rounded up to a multiple of 32, i.e. 4 bytes per (sequence,
+ * KV head, padded key block, dim).  0 on an invalid problem. */
 size_t cosa_kap_workspace_size(const cosa_problem* p);
 
 /* Host-side check of a host copy of cu_seqlens [batch+1] and page_table
