@@ -420,6 +420,7 @@ __global__ __launch_bounds__(NW * HP * 64, (PPB == 1 && HP == 1) ? 2 : 1) void a
   float m_ref = kNegInf;    // reference max of the exponentials (<= m_true)
   float lsum = 0.f;         // this lane's half of the running sum, relative to m_ref
   int nskip = 0;
+  bool v_have = true;       // the V page(s) of the current slot were prefetched
   uint32_t rec_word = 0;    // skip bits of the head's current 32 slots
   const bool skip_on = kOrdered && p.skip_mode != kSkipOff;
   // threshold in log2 units: fixed, or log2(L / Delta) for this sequence
@@ -636,9 +637,21 @@ __global__ __launch_bounds__(NW * HP * 64, (PPB == 1 && HP == 1) ? 2 : 1) void a
       copy_k(tk, slot_block(tk), st);
       copy_v(tv, slot_block(tv), st_prev);
     } else {
+      // A skipped block needs no V page.  Skips come in runs (once the row
+      // maxima are found, most later blocks fall below them), so V(t+1) is
+      // prefetched only after a computed block; a computed block whose V was
+      // not prefetched fetches it here, before the other copies, and waits.
+      if (sel && !skip && !v_have) {   // uniform over the workgroup
+        copy_v(t, j_cur, st);
+        wait_vm_c<0>();
+        lds_barrier();
+      }
       if (t + NS < cnt && selected(t + NS)) copy_k(t + NS, slot_block(t + NS), st);
-      if (t + NS - 1 < cnt && selected(t + NS - 1))
+      v_have = false;
+      if (t + NS - 1 < cnt && selected(t + NS - 1) && !skip) {
         copy_v(t + NS - 1, slot_block(t + NS - 1), st_prev);
+        v_have = true;
+      }
     }
 
     if (sel && key0 + KVB > L) {   // uniform: the sequence's last block
