@@ -75,12 +75,27 @@ def _rows(path):
         return list(csv.DictReader(f))
 
 
+def _workgroups(r):
+    """Workgroups of a dispatch record (None when the CSV has no sizes)."""
+    if "Grid_Size" not in r or "Workgroup_Size" not in r:
+        return None
+    return int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+
+
 def per_kernel_counter(path):
-    """{(kernel, counter): [values per dispatch]} from a counter_collection CSV."""
+    """{((kernel, workgroups), counter): [values per dispatch]} from a
+    counter_collection CSV: launches of one kernel over different parts of
+    the work (the chunks of the fused call) are kept apart."""
     agg = collections.defaultdict(list)
     for r in _rows(path):
-        agg[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+        agg[((r["Kernel_Name"], _workgroups(r)), r["Counter_Name"])].append(
+            float(r["Counter_Value"]))
     return agg
+
+
+def _label(kw):
+    k, wg = kw
+    return f"`{short_name(k)}`" + ("" if wg is None else f" | {wg}")
 
 
 def stats_md(path, command):
@@ -112,7 +127,7 @@ def trace_md(path, command):
 def _copy_kib(path, counter):
     """Largest per-dispatch value of ``counter`` for the device copy kernel."""
     best = 0.0
-    for (k, c), v in per_kernel_counter(path).items():
+    for ((k, _), c), v in per_kernel_counter(path).items():
         if c == counter and "copyBuffer" in k:
             best = max(best, max(v))
     if best <= 0:
@@ -128,21 +143,23 @@ def traffic_md(fetch, write, cfetch, cwrite, copy_bytes, workload, budget, tau, 
     lines = [f"Command: `{command}`", "",
              f"Copy calibration ({copy_bytes} B device copy): FETCH_SIZE x{f_scale:.3f}, "
              f"WRITE_SIZE x{w_scale:.3f} to reach true bytes.", "",
-             "| kernel | dispatches | FETCH KiB (raw) | WRITE KiB (raw) | read GB (scaled) | "
-             "written GB (scaled) | total GB |", "|---|---|---|---|---|---|---|"]
+             "| kernel | workgroups | dispatches | FETCH KiB (raw) | WRITE KiB (raw) | "
+             "read GB (scaled) | written GB (scaled) | total GB |",
+             "|---|---|---|---|---|---|---|---|"]
     records = []
-    for (k, c), v in sorted(fr.items()):
+    for (kw, c), v in sorted(fr.items(), key=lambda kv: (kv[0][0][0], -(kv[0][0][1] or 0))):
+        k, wg = kw
         if c != "FETCH_SIZE" or "cosa" not in k:
             continue
-        wv = wr.get((k, "WRITE_SIZE"))
+        wv = wr.get((kw, "WRITE_SIZE"))
         if not wv:
             continue
         fk, wk = sum(v) / len(v), sum(wv) / len(wv)
         rd, wt = fk * 1024 * f_scale, wk * 1024 * w_scale
-        lines.append(f"| `{short_name(k)}` | {len(v)} | {fk:.6g} | {wk:.6g} | {rd / 1e9:.3f} | "
-                     f"{wt / 1e9:.3f} | {(rd + wt) / 1e9:.3f} |")
+        lines.append(f"| `{short_name(k)}` | {wg} | {len(v)} | {fk:.6g} | {wk:.6g} | "
+                     f"{rd / 1e9:.3f} | {wt / 1e9:.3f} | {(rd + wt) / 1e9:.3f} |")
         if "attn_fwd_kernel" in k:
-            records.append({"kernel": short_name(k), "entry": entry_of(k),
+            records.append({"kernel": short_name(k), "entry": entry_of(k), "workgroups": wg,
                             "workload": workload, "budget": budget,
                             "tau": tau, "read_bytes": round(rd), "write_bytes": round(wt),
                             "bytes_per_launch": round(rd + wt), "source_digest": digest})
@@ -153,29 +170,32 @@ def traffic_md(fetch, write, cfetch, cwrite, copy_bytes, workload, budget, tau, 
 
 def counters_md(path, command, xcds=8, simds=1024):
     agg = per_kernel_counter(path)
-    kernels = sorted({k for k, _ in agg if "cosa" in k})
+    kernels = sorted({kw for kw, _ in agg if "cosa" in kw[0]},
+                     key=lambda kw: (kw[0], -(kw[1] or 0)))
     names = sorted({c for _, c in agg})
     out = [f"Command: `{command}`", "",
-           "| kernel | " + " | ".join(names) + " | MfmaUtil |",
-           "|---|" + "---|" * (len(names) + 1)]
+           "| kernel | workgroups | " + " | ".join(names) + " | MfmaUtil |",
+           "|---|---|" + "---|" * (len(names) + 1)]
     for k in kernels:
         vals = {c: sum(agg[(k, c)]) / len(agg[(k, c)]) for c in names if (k, c) in agg}
         util = ""
         if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and vals.get("GRBM_GUI_ACTIVE"):
             # GRBM_GUI_ACTIVE is summed over the XCDs; busy cycles over the SIMDs
             util = f"{vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (vals['GRBM_GUI_ACTIVE'] / xcds * simds):.3f}"
-        out.append(f"| `{short_name(k)}` | " +
+        out.append(f"| `{short_name(k[0])}` | {k[1]} | " +
                    " | ".join(f"{vals[c]:.4g}" if c in vals else "" for c in names) +
                    f" | {util} |")
     return "\n".join(out)
 
 
 def read_traffic(path, workload, budget, tau):
-    """Bytes per launch recorded for the attention kernel with these settings,
-    or None when absent or taken on different kernel sources."""
+    """Bytes per launch recorded for the whole-layer attention launch with these
+    settings (the largest grid of cosa_osk_prefill's kernel), or None when
+    absent or taken on different kernel sources."""
     if not os.path.exists(path):
         return None
     digest = attention_source_digest()
+    best = None
     with open(path) as f:
         for line in f:
             if not line.startswith("bench-traffic: "):
@@ -184,8 +204,9 @@ def read_traffic(path, workload, budget, tau):
             if (r.get("entry") == "cosa_osk_prefill" and r["workload"] == workload and
                     abs(r["budget"] - budget) < 1e-9 and abs(r["tau"] - tau) < 1e-9 and
                     r["source_digest"] == digest):
-                return r
-    return None
+                if best is None or (r.get("workgroups") or 0) > (best.get("workgroups") or 0):
+                    best = r
+    return best
 
 
 def main(argv=None):

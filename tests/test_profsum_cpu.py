@@ -77,3 +77,30 @@ def test_trace_groups_launches_by_grid(tmp_path):
     assert len(lines) == 2
     assert "| 32 | 2 | 3.0000 | 2.0000 | 4.0000 | 6.000 |" in lines[0]
     assert "| 4 | 1 | 0.5000 |" in lines[1]
+
+
+def test_traffic_keeps_launch_sizes_apart(tmp_path):
+    attn = "void cosa::(anonymous namespace)::attn_fwd_kernel<128, 4, 1, 1, 1, 2>(cosa::AttnParams)"
+
+    def rows(path, counter, vals):
+        with open(path, "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(["Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Name",
+                        "Counter_Value"])
+            for name, grid, v in vals:
+                w.writerow([name, grid, 256, counter, v])
+
+    # two whole-layer launches (8 workgroups) and two chunk launches (1 workgroup)
+    rows(tmp_path / "f.csv", "FETCH_SIZE", [(attn, 2048, 800.0), (attn, 2048, 800.0),
+                                            (attn, 256, 100.0), (attn, 256, 100.0)])
+    rows(tmp_path / "w.csv", "WRITE_SIZE", [(attn, 2048, 80.0), (attn, 256, 10.0)])
+    rows(tmp_path / "cf.csv", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 512, 512.0)])
+    rows(tmp_path / "cw.csv", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 512, 1024.0)])
+    md = profsum.traffic_md(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                            str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), 1024 * 1024,
+                            "wl", 0.1, 8.0, "cmd")
+    prof = tmp_path / "p.md"
+    prof.write_text(md)
+    r = profsum.read_traffic(str(prof), "wl", 0.1, 8.0)
+    assert r["workgroups"] == 8
+    assert r["read_bytes"] == 1600 * 1024 and r["write_bytes"] == 80 * 1024
