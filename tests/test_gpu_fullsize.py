@@ -54,6 +54,17 @@ def test_full_layer_sampled_parity(name, n_samples):
     m = bk.proxy_ordered_mask(prob, q, k, w.budget)
     r = bk.osk_prefill(prob, q, k, v, m, w.tau)
     torch.cuda.synchronize()
+    # the fused call at full size, the kernel on a second stream: same bits
+    print(f"[case] full-size {name}: fused call", flush=True)
+    fm, fr = bk.sparse_prefill(prob, q, k, v, w.budget, w.tau,
+                               aux_stream=torch.cuda.Stream(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(fm.blocks, m.blocks) and torch.equal(fm.counts, m.counts)
+    assert torch.equal(fm.pages, m.pages) and torch.equal(fm.hrm_counts, m.hrm_counts)
+    assert torch.equal(fr.out.view(torch.int16), r.out.view(torch.int16))
+    assert torch.equal(fr.lse.view(torch.int32), r.lse.view(torch.int32))
+    assert torch.equal(fr.row_stats, r.row_stats)
+    del fm, fr
     gb, gp, gc, gh = _np(m.blocks), _np(m.pages), _np(m.counts), _np(m.hrm_counts)
     out, lse, rec, stats = _np(r.out), _np(r.lse), _np(r.skip_record), _np(r.row_stats)
     del r
