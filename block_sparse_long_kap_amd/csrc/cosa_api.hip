@@ -372,6 +372,7 @@ COSA_EXPORT cosa_status cosa_sparse_prefill(
   auto cleanup = [&]() {
     for (int x = 0; x < n_ev; ++x) (void)hipEventDestroy(ev[x]);
   };
+  bool used_aux = false;
   for (int g0 = 0; g0 < n_groups; g0 += chunk) {
     const int cnt = n_groups - g0 < chunk ? n_groups - g0 : chunk;
     k.group_begin = a.group_begin = g0;
@@ -387,18 +388,21 @@ COSA_EXPORT cosa_status cosa_sparse_prefill(
       if (e == hipSuccess) e = hipStreamWaitEvent(s1, ev[n_ev - 1], 0);
       if (e != hipSuccess) break;
       s_attn = s1;
+      used_aux = true;
     }
     e = cosa::launch_attention(a, p->head_dim, p->q_block, cosa::kModeOrdered, s_attn);
     if (e != hipSuccess) break;
   }
-  if (e == hipSuccess && s1 != nullptr) {
-    // the caller's stream continues after the last chunk's kernel
-    e = hipEventCreateWithFlags(&ev[n_ev], hipEventDisableTiming);
-    if (e == hipSuccess) {
+  if (used_aux) {
+    // the caller's stream continues after the last kernel on aux_stream (also
+    // after an error, so that nothing of this call is left unordered)
+    hipError_t ej = hipEventCreateWithFlags(&ev[n_ev], hipEventDisableTiming);
+    if (ej == hipSuccess) {
       ++n_ev;
-      e = hipEventRecord(ev[n_ev - 1], s1);
-      if (e == hipSuccess) e = hipStreamWaitEvent(s0, ev[n_ev - 1], 0);
+      ej = hipEventRecord(ev[n_ev - 1], s1);
+      if (ej == hipSuccess) ej = hipStreamWaitEvent(s0, ev[n_ev - 1], 0);
     }
+    if (e == hipSuccess) e = ej;
   }
   cleanup();
   return hip_status(e);
