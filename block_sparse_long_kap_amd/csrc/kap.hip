@@ -25,9 +25,9 @@
 //                  per-row max / arg-max / sum online in a first pass,
 //                  recomputes the scores for the weights in a second pass,
 //                  builds 64-bit keys (not HRM, -w, j) in LDS, radix-selects
-//                  the k smallest per tile (one wavefront per tile), bitonic-
-//                  sorts only those and writes the first k ids of each tile
-//                  with their remapped pages.
+//                  the k smallest per tile and bitonic-sorts only those (one
+//                  wavefront per tile, no workgroup barrier), and writes the
+//                  first k ids of each tile with their remapped pages.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -163,19 +163,23 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   constexpr int KCH = D / 8;
   static_assert(MR <= 32, "one 32-row MFMA operand");
 
-  // 16 KB of sort keys per tile; the pooled queries (2 x 32 x D bf16) live in
-  // the same space before the keys are built
-  __shared__ __attribute__((aligned(16))) unsigned long long sKey[TPW][kMaxCandidates];
-  __shared__ RowStat sStat[NWAVE][32];
+  // 16 KB of sort keys per tile.  Before the keys are built the same space
+  // holds the pooled queries (2 x 32 x D bf16), then the per-lane partial row
+  // statistics of pass 1 (max, sum, arg-max: 32 rows x kPartStride each; the
+  // stride spreads a row's partials over the LDS banks).
+  constexpr int kPartStride = 32 * NWAVE + 8;
+  constexpr int kKeyWords = TPW * kMaxCandidates;
+  constexpr int kPartWords = (3 * 32 * kPartStride + 1) / 2;
+  __shared__ __attribute__((aligned(16)))
+  unsigned long long sKeyRaw[kKeyWords > kPartWords ? kKeyWords : kPartWords];
+  auto sKey = reinterpret_cast<unsigned long long (*)[kMaxCandidates]>(sKeyRaw);
   __shared__ float sRowM[32];
   __shared__ float sRowInvZ[32];
-  __shared__ int sRowA[32];
   __shared__ int sHrm[TPW];          // HRM keys per tile
-  __shared__ int sSel[TPW];          // keys kept by the selection
   __shared__ int sTopK[TPW];         // Top-p: kept count per tile
   __shared__ uint32_t sHist[NWAVE][256];
   __shared__ unsigned long long sMass[kTopP ? NWAVE : 1][256];   // Top-p only
-  uint16_t* sQhi = reinterpret_cast<uint16_t*>(&sKey[0][0]);
+  uint16_t* sQhi = reinterpret_cast<uint16_t*>(sKeyRaw);
   uint16_t* sQlo = sQhi + 32 * D;
 
   const int tid = threadIdx.x;
@@ -309,6 +313,10 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     ahi[ks] = *reinterpret_cast<const bf16x8_t*>(&sQhi[col * D + ks * 16 + hf * 8]);
     alo[ks] = *reinterpret_cast<const bf16x8_t*>(&sQlo[col * D + ks * 16 + hf * 8]);
   }
+  // every wave holds its operand before any wave writes the partial row
+  // statistics into the same LDS space (a wave without candidate blocks
+  // writes them right away)
+  __syncthreads();
   // rows held by this lane's accumulator registers: m = 8(r/4) + 4hf + r%4
   int cand[16];
 #pragma unroll
@@ -321,8 +329,8 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   const int nb = (n_wg + 31) / 32;
 
   // pooled-key operands of candidate block cb (B of the score product); a
-  // wave loads its next block right after the current block's products, so
-  // the loads travel while the row statistics are updated
+  // wave loads a block while the products of the block before it run and
+  // the statistics of the one before that are updated
   bf16x8_t kh[KSTEPS], kl[KSTEPS];
   // (blocks past the sequence's last one hold stale values; their scores
   // are masked)
@@ -355,10 +363,11 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   RowStat st[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) st[r] = RowStat{kNegInf, 0.f, 0x7FFFFFFF};
-  if (wave < nb) load_ops(wave);
-  for (int cb = wave; cb < nb; cb += NWAVE) {
-    const f32x16_t acc = scores();
-    if (cb + NWAVE < nb) load_ops(cb + NWAVE);
+  // software-pipelined: the products of block cb + NWAVE are issued before
+  // the statistics of block cb, whose vector work then overlaps them, and
+  // the operands of block cb + 2 NWAVE are loaded meanwhile (near the end
+  // the index is clamped to the last block; that load goes unused)
+  auto stats1 = [&](const f32x16_t& acc, int cb) {
     const int j = cb * 32 + col;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -375,33 +384,68 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
       st[r].a = valid && up ? j : st[r].a;
       st[r].m = valid && up ? s : st[r].m;
     }
+  };
+  f32x16_t acc_cur = {};
+  if (wave < nb) {
+    load_ops(wave);
+    acc_cur = scores();
+    if (wave + NWAVE < nb) load_ops(wave + NWAVE);
   }
-  // merge over the 32 candidate lanes of each half, then over the waves
+  int cb1 = wave;
+  for (; cb1 + NWAVE < nb; cb1 += NWAVE) {
+    const f32x16_t acc_next = scores();
+    load_ops(min(cb1 + 2 * NWAVE, nb - 1));
+    stats1(acc_cur, cb1);
+    acc_cur = acc_next;
+  }
+  if (cb1 < nb) stats1(acc_cur, cb1);
+  // merge the 128 partial statistics of every row (32 candidate lanes x
+  // NWAVE waves): each lane puts its 16 rows' partials into LDS, then eight
+  // threads per row merge 16 partials each (max first, then the sum rescaled
+  // to it and the lowest block index reaching it) and combine over three
+  // lane steps
+  float* sPm = reinterpret_cast<float*>(sKeyRaw);
+  float* sPz = sPm + 32 * kPartStride;
+  int* sPa = reinterpret_cast<int*>(sPz + 32 * kPartStride);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) {
-      RowStat o;
-      o.m = __shfl_xor(st[r].m, off);
-      o.z = __shfl_xor(st[r].z, off);
-      o.a = __shfl_xor(st[r].a, off);
-      st[r] = merge(st[r], o);
-    }
-  }
-  if (col == 0) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sStat[wave][8 * (r >> 2) + 4 * hf + (r & 3)] = st[r];
+    const int at = (8 * (r >> 2) + 4 * hf + (r & 3)) * kPartStride + wave * 32 + col;
+    sPm[at] = st[r].m;
+    sPz[at] = st[r].z;
+    sPa[at] = st[r].a;
   }
   __syncthreads();
-  if (tid < 32) {
-    RowStat s = sStat[0][tid];
-    for (int w = 1; w < NWAVE; ++w) s = merge(s, sStat[w][tid]);
-    sRowM[tid] = s.m;
-    sRowInvZ[tid] = s.z > 0.f ? 1.f / s.z : 0.f;
-    sRowA[tid] = s.m == kNegInf ? -1 : s.a;
-    if (s.m != kNegInf && tid < MR) {
-      const int t = tid / RPT;
-      atomicOr(&sHrmBits[t * (kMaxCandidates / 32) + (s.a >> 5)], 1u << (s.a & 31));
+  {
+    constexpr int PER = 32 * NWAVE / 8;
+    const int row = tid >> 3;
+    const int base = row * kPartStride + (tid & 7);
+    float mx = kNegInf;
+#pragma unroll
+    for (int x = 0; x < PER; ++x) mx = fmaxf(mx, sPm[base + 8 * x]);
+    RowStat s{mx, 0.f, 0x7FFFFFFF};
+    if (mx != kNegInf) {
+#pragma unroll
+      for (int x = 0; x < PER; ++x) {
+        const float mi = sPm[base + 8 * x];
+        if (mi != kNegInf) s.z += sPz[base + 8 * x] * __builtin_amdgcn_exp2f(mi - mx);
+        if (mi == mx) s.a = min(s.a, sPa[base + 8 * x]);
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      RowStat o;
+      o.m = __shfl_xor(s.m, off);
+      o.z = __shfl_xor(s.z, off);
+      o.a = __shfl_xor(s.a, off);
+      s = merge(s, o);
+    }
+    if ((tid & 7) == 0) {
+      sRowM[row] = s.m;
+      sRowInvZ[row] = s.z > 0.f ? 1.f / s.z : 0.f;
+      if (s.m != kNegInf && row < MR) {
+        const int t = row / RPT;
+        atomicOr(&sHrmBits[t * (kMaxCandidates / 32) + (s.a >> 5)], 1u << (s.a & 31));
+      }
     }
   }
   __syncthreads();
@@ -414,8 +458,6 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     rm[r] = sRowM[m];
     riz[r] = sRowInvZ[m];
   }
-  int npow = 1;
-  while (npow < n_wg) npow <<= 1;
   if (tid < TPW) sHrm[tid] = 0;
   __syncthreads();
 
@@ -433,13 +475,11 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
       if (p.debug_w != nullptr) p.debug_w[row * p.n_max + j] = w;
       if (p.debug_hrm != nullptr) p.debug_hrm[row * p.n_max + j] = hrm ? 1 : 0;
     }
-    if (j < npow) sKey[t][j] = key;
+    sKey[t][j] = key;   // j < nb * 32 <= kMaxCandidates
   };
 
-  if (wave < nb) load_ops(wave);
-  for (int cb = wave; cb < nb; cb += NWAVE) {
-    const f32x16_t acc = scores();
-    if (cb + NWAVE < nb) load_ops(cb + NWAVE);
+  // software-pipelined like pass 1
+  auto weights = [&](const f32x16_t& acc, int cb) {
     const int j = cb * 32 + col;
     float part[4];
 #pragma unroll
@@ -469,12 +509,21 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
 #pragma unroll
       for (int g4 = 0; g4 < 2; ++g4) emit(2 * g4 + hf, j, part[g4]);
     }
+  };
+  acc_cur = (f32x16_t){};
+  if (wave < nb) {
+    load_ops(wave);
+    acc_cur = scores();
+    if (wave + NWAVE < nb) load_ops(wave + NWAVE);
   }
-  // padding keys up to the power of two
-  for (int idx = tid; idx < TPW * npow; idx += NT) {
-    const int t = idx / npow, j = idx - (idx / npow) * npow;
-    if (j >= nb * 32) sKey[t][j] = ~0ull;
+  int cb2 = wave;
+  for (; cb2 + NWAVE < nb; cb2 += NWAVE) {
+    const f32x16_t acc_next = scores();
+    load_ops(min(cb2 + 2 * NWAVE, nb - 1));
+    weights(acc_cur, cb2);
+    acc_cur = acc_next;
   }
+  if (cb2 < nb) weights(acc_cur, cb2);
   __syncthreads();
 
   // ---- 5) top-k selection per tile (wave t handles tile t): radix-select
@@ -498,6 +547,16 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     const int n = n_t[t];
     int k = k_t[t];
     int sel = n;                              // keys kept for the final sort
+    // upper key halves (HRM flag, -w) of the tile, lane + 64e, in registers
+    // for the radix rounds
+    constexpr int kPerLane = kMaxCandidates / 64;
+    uint32_t hk[kPerLane];
+    const uint32_t* khalf = reinterpret_cast<const uint32_t*>(&sKey[t][0]);
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) {
+      const int idx = lane + 64 * e;
+      hk[e] = idx < n ? khalf[2 * idx + 1] : 0u;
+    }
     uint32_t top_prefix = 0;
     bool top_bound = false;                   // the Top-p count decides k
     if (kTopP && n > 0 && k > 1) {
@@ -515,9 +574,11 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
           sHist[t][bin] = 0;
           sMass[t][bin] = 0ull;
         }
-        for (int idx = lane; idx < n; idx += 64) {
-          const uint32_t hi = (uint32_t)(sKey[t][idx] >> 32);
-          if ((hi & pmask) == prefix) {
+#pragma unroll
+        for (int e = 0; e < kPerLane; ++e) {
+          if (64 * e >= n) break;
+          const uint32_t hi = hk[e];
+          if (lane + 64 * e < n && (hi & pmask) == prefix) {
             const uint32_t d = (hi >> shift) & 255u;
             atomicAdd(&sHist[t][d], 1u);
             atomicAdd(&sMass[t][d], key_mass(hi));
@@ -585,9 +646,11 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
       int need = k;
       for (int shift = 24; shift >= 0 && !top_bound; shift -= 8) {
         for (int bin = lane; bin < 256; bin += 64) sHist[t][bin] = 0;
-        for (int idx = lane; idx < n; idx += 64) {
-          const uint32_t hi = (uint32_t)(sKey[t][idx] >> 32);
-          if ((hi & pmask) == prefix) atomicAdd(&sHist[t][(hi >> shift) & 255u], 1u);
+#pragma unroll
+        for (int e = 0; e < kPerLane; ++e) {
+          if (64 * e >= n) break;
+          if (lane + 64 * e < n && (hk[e] & pmask) == prefix)
+            atomicAdd(&sHist[t][(hk[e] >> shift) & 255u], 1u);
         }
         uint32_t c[4];
 #pragma unroll
@@ -629,43 +692,36 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
       }
       sel = written;
     }
-    if (lane == 0) sSel[t] = sel;
+
+    // ---- 6) bitonic sort of the kept keys, ascending, by this wavefront
+    // alone (LDS operations of one wavefront complete in order, so a step
+    // sees the writes of the step before it without a workgroup barrier)
+    int npow = 1;
+    while (npow < sel) npow <<= 1;
+    for (int j = sel + lane; j < npow; j += 64) sKey[t][j] = ~0ull;
+    const int half = npow >> 1;
+    for (int size = 2; size <= npow; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        for (int q = lane; q < half; q += 64) {
+          const int lo = ((q & ~(stride - 1)) << 1) | (q & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const unsigned long long a = sKey[t][lo], c = sKey[t][hi];
+          if ((a > c) == up) {
+            sKey[t][lo] = c;
+            sKey[t][hi] = a;
+          }
+        }
+      }
+    }
   }
   __syncthreads();
   if (kTopP) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
       if (n_t[t] > 0 && k_t[t] > 1) k_t[t] = sTopK[t];
-  }
-  int npow_sel = 1;
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-    while (npow_sel < sSel[t]) npow_sel <<= 1;
-  for (int idx = tid; idx < TPW * npow_sel; idx += NT) {
-    const int t = idx / npow_sel, j = idx - t * npow_sel;
-    if (j >= sSel[t]) sKey[t][j] = ~0ull;
-  }
-  __syncthreads();
-
-  // ---- 6) bitonic sort of the TPW selections together, ascending
-  const int half = npow_sel >> 1;
-  const int lhalf = 31 - __clz(max(half, 1));
-  for (int size = 2; size <= npow_sel; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int pi = tid; pi < TPW * half; pi += NT) {
-        const int t = pi >> lhalf;
-        const int q = pi & (half - 1);
-        const int lo = ((q & ~(stride - 1)) << 1) | (q & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const unsigned long long a = sKey[t][lo], c = sKey[t][hi];
-        if ((a > c) == up) {
-          sKey[t][lo] = c;
-          sKey[t][hi] = a;
-        }
-      }
-      __syncthreads();
-    }
   }
 
   // ---- 7) first k entries of every tile, remapped pages, counts
