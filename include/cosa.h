@@ -17,10 +17,11 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * Pointers named "device" point to GPU memory; the library never allocates,
- * frees or synchronises, keeps no state between calls and enqueues all of its
- * work on the caller's stream (``stream`` is a hipStream_t; NULL is the
- * default stream).  The caller owns every buffer.  Arguments are validated on
+ * Pointers named "device" point to GPU memory; the library never allocates
+ * or frees device memory and never synchronises the host, keeps no state
+ * between calls (apart from each host thread's last error message, see
+ * cosa_last_error()) and enqueues all of its work on the caller's stream
+ * (``stream`` is a hipStream_t; NULL is the default stream).  The caller owns every buffer.  Arguments are validated on
  * the host before any launch: an invalid call returns an error status and
  * enqueues nothing.  A launch failure returns COSA_ERR_HIP.  Only host-side
  * values are checked; device contents (page ids, sequence lengths in
