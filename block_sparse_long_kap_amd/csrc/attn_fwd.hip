@@ -3,7 +3,7 @@
 //
 // Method: CoSA (paper text on paperpeel.com), §4.3 "Ordered-Skipping Kernel":
 // the kernel follows the computation-order mask by remapping pages of the
-// paged KV cache (physical jumping, any-order page visiting) and applies the
+// paged KV cache (it jumps to each physical page, in any order) and applies the
 // in-kernel skip of §3.3 Eq. (5) at the granularity of one query tile
 // (App. D.1: one tile-wide vote combined from the row-wise predicates, made
 // from the on-chip online-softmax maxima with no extra logits and no extra

@@ -8,10 +8,11 @@
  *     every query block and emits a computation-order mask M_KAP, with the
  *     "have rowmax" (HRM) blocks first, truncated to a stage-1 budget;
  *   - the Ordered-Skipping Kernel (OSK, §4.3) visits only the pages of that
- *     mask, in its order, through the page table ("physical jumping over
- *     pages", "any-order page visiting"), and skips the value-side work of a
- *     block from the exact online-softmax statistics ("in-kernel logic skip",
- *     §3.3 Eq. (5)) with one vote per query tile (App. D.1);
+ *     mask, in its order, through the page table (it jumps straight to each
+ *     physical page and may take them in any order), and skips the
+ *     value-side work of a block when the exact online-softmax statistics
+ *     show it negligible (§3.3 Eq. (5)), with one vote per query tile
+ *     (App. D.1);
  *   - dense causal prefill (§3.1; the full-attention baseline of §5.1) runs on
  *     the same kernel with every causal block visited in ascending order.
  *
