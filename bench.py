@@ -15,9 +15,14 @@ heads, head_dim 128, 131072 tokens, query tile 128, KV page 64, shuffled page
 table, planted sink / band / stripe structure).
 
 Prints one JSON line (rank 0).  Times are HIP-event times on the stream the
-kernels run on; ``roofline`` describes the dominant kernel (the OSK);
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same layer
-and extrapolates to the whole layer.
+kernels run on; ``roofline`` describes the dominant kernel (the OSK) against
+the bf16 MFMA peak: algorithmic FLOP per launch (2 * 128 * 64 * 128 per
+visited block for the logits, the same per computed block for P V) over the
+launch's average time.  ``stage2`` times the same layer on ``remap128k``, a
+128K input of the same shape on which the in-kernel skip fires (on llama128k
+no tile is ever skipped), with the skip on and off.  ``cpu_baseline`` times
+the CPU oracle on a bounded sample of the same layer and extrapolates to the
+whole layer.
 """
 from __future__ import annotations
 
@@ -62,6 +67,8 @@ def parse():
     ap.add_argument("--logical-skip", action="store_true",
                     help="also time physical page jumping (OSK, skip off) against logical mask "
                          "skipping (cosa_block_mask_prefill) on the same kept sets (extra lines)")
+    ap.add_argument("--no-stage2", action="store_true",
+                    help="skip the in-kernel-skip measurement on the remap128k input")
     ap.add_argument("--shared-kv", action="store_true",
                     help="also time the KAP + OSK with one mask per KV head shared by its query "
                          "heads (extra JSON line)")
@@ -98,8 +105,8 @@ def main():
     import torch
 
     import block_sparse_long_kap_amd as bk
-    from block_sparse_long_kap_amd import profsum
     import cosa_inputs as ci
+    import profsum
     from block_sparse_long_kap_amd import _lib
 
     _lib.load()
@@ -231,13 +238,15 @@ def main():
         dense_ms = d0.elapsed_time(d1) / nd
 
     osk_tflops = osk_flops / (osk_ms * 1e-3) / 1e12 if osk_ms > 0 else 0.0
-    # bytes the OSK moves by definition: the K and V page of every visited
-    # (tile, block) slot, the query tile read and the output tile written
+    # secondary view: the bytes of the OSK's page stream, the K and V page of
+    # every visited (tile, block) slot plus the query tile read and the
+    # output tile written (per-tile re-reads included; part of them hit L2)
     n_tiles = w.num_q_heads * int(sum(-(-int(L) // w.q_block) for L in lens))
     osk_bytes = osk_slot_bytes(w) * visited + osk_tile_bytes(w) * n_tiles
     osk_gbs = osk_bytes / (osk_ms * 1e-3) / 1e9 if osk_ms > 0 else 0.0
     # HBM bytes per OSK launch from the committed rocprofv3 counter summary,
     # only while it was taken on the current kernel sources and settings
+    # (not measured in this run; null once the kernel has changed)
     traffic = profsum.read_traffic(os.path.join(ROOT, TRAFFIC_PROFILE), w.name, budget, tau)
     kap_bytes = (q.numel() * 2 + (w.total_tokens * w.num_kv_heads * w.head_dim * 2)
                  + 2 * mask.blocks.numel() * 4 + mask.counts.numel() * 8)
@@ -278,22 +287,32 @@ def main():
         "effective_budget": round(computed / causal_slots, 5),
         "wall_ms_timed_region": round(wall_ms, 2),
         "input_gen_s": round(gen_s, 1),
-        # The OSK at these budgets is bound by its page stream (each tile
-        # gathers its own K and V pages): achieved = algorithmic bytes per
-        # launch / launch time, next to the MFMA view of the same launch.
-        "roofline": {"bound": "hbm", "achieved": round(osk_gbs, 1),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(osk_gbs / PEAK_HBM_GBS, 4),
+        # The OSK's roofline: bf16 MFMA, algorithmic FLOP per launch (logits
+        # of every visited block, P V of every computed one) over the average
+        # launch time of the timed loop.  The page stream's bytes and the
+        # counter-measured traffic are secondary fields.
+        "roofline": {"bound": "mfma", "achieved": round(osk_tflops, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(osk_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
-                     "traffic_unit": "bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1)",
-                     "traffic_source": None if traffic is None else TRAFFIC_PROFILE,
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1)",
+                     "traffic_source": None if traffic is None else
+                     TRAFFIC_PROFILE + " (rocprofv3 --pmc on the same kernel sources; "
+                     "not measured in this run)",
                      "kernel": "attn_fwd_kernel<128, 4, 1, 1, 1, 2> (cosa_osk_prefill)",
-                     "algorithmic_bytes_per_launch": osk_bytes,
+                     "launch_ms": round(osk_ms, 4),
                      "algorithmic_flop_per_launch": osk_flops,
-                     "mfma_tflops": round(osk_tflops, 1),
-                     "mfma_frac": round(osk_tflops / PEAK_BF16_TFLOPS, 4)},
+                     "page_stream": {"bytes_per_launch": osk_bytes,
+                                     "gbs": round(osk_gbs, 1),
+                                     "frac_of_hbm_peak": round(osk_gbs / PEAK_HBM_GBS, 4),
+                                     "note": "K+V page of every visited (tile, block) slot "
+                                             "plus Q/out tiles; per-tile re-reads counted"}},
+        "stage2": None,
         "cpu_baseline": None,
     }
+    if not args.no_stage2 and args.only == "all":
+        result["stage2"] = stage2_measurement(args, bk, torch, dev, stream, ev, dense_ms,
+                                              w.name)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x, budget, tau, args.cpu_tiles)
     print(json.dumps(result), flush=True)
@@ -366,6 +385,77 @@ def main():
                               "skip_ratio": round(skp / max(vis, 1), 5),
                               "effective_budget": round((vis - skp) / causal_slots, 5),
                               "osk_tflops": round(fl / om / 1e9, 1)}), flush=True)
+
+
+STAGE2_WORKLOAD = "remap128k"
+
+
+def stage2_measurement(args, bk, torch, dev, stream, ev, dense_ms, headline):
+    """The in-kernel skip at 128K: proxy + OSK on the remap128k input (the
+    Llama shape with a strong local band and no sink, so that whole tiles
+    fall tau below their running max) at its budget and tau, timed as two
+    calls like kap_ms / osk_ms, and the OSK again on the same mask with the
+    skip off.  The dense kernel's time on the headline input of the same
+    shape is the speedup baseline (dense work does not depend on values)."""
+    import cosa_inputs as ci
+    w = ci.get(STAGE2_WORKLOAD)
+    x = ci.make(w)
+    q = torch.from_numpy(x.q).to(torch.bfloat16).to(dev)
+    kp = torch.from_numpy(x.k_pool).to(torch.bfloat16).to(dev)
+    vp = torch.from_numpy(x.v_pool).to(torch.bfloat16).to(dev)
+    prob = bk.Problem(cu_seqlens=torch.from_numpy(x.cu_seqlens).to(dev),
+                      page_table=torch.from_numpy(x.page_table).to(dev),
+                      num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                      head_dim=w.head_dim, max_seqlen=w.max_seqlen, total_q=w.total_tokens,
+                      num_pages=x.k_pool.shape[0], q_block=w.q_block, page_size=w.page_size,
+                      softmax_scale=w.softmax_scale)
+    lens = np.diff(x.cu_seqlens)
+    del x
+    ws = bk.KapWorkspace(prob)
+    mask = bk.proxy_ordered_mask(prob, q, kp, w.budget, workspace=ws)
+    rec = bk.osk_prefill(prob, q, kp, vp, mask, w.tau, record=True)
+    out = bk.PrefillOutput(out=torch.empty_like(q), lse=torch.empty_like(rec.lse))
+    torch.cuda.synchronize()
+    st = rec.row_stats.cpu().numpy().reshape(-1, 2)
+    del rec
+    vis, skp = int(st[:, 0].sum()), int(st[:, 1].sum())
+    causal = 0
+    for L in lens:
+        for i in range((int(L) + w.q_block - 1) // w.q_block):
+            causal += (min((i + 1) * w.q_block, int(L)) - 1) // w.page_size + 1
+    causal *= w.num_q_heads
+    fps = flops_per_slot(w.q_block, w.head_dim, w.page_size)
+
+    def timed(fn, n):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    kap_ms = timed(lambda: bk.proxy_ordered_mask(prob, q, kp, w.budget, workspace=ws,
+                                                 out=mask), args.steps)
+    osk_ms = timed(lambda: bk.osk_prefill(prob, q, kp, vp, mask, w.tau, out=out), args.steps)
+    off_ms = timed(lambda: bk.osk_prefill(prob, q, kp, vp, mask, -1.0, out=out), args.steps)
+    flop = fps * (2 * vis - skp)
+    tf = flop / (osk_ms * 1e-3) / 1e12
+    return {"workload": w.name, "budget": w.budget, "tau": w.tau, "seed": w.seed,
+            "kap_ms": round(kap_ms, 4), "osk_ms": round(osk_ms, 4),
+            "ms_per_layer_two_calls": round(kap_ms + osk_ms, 4),
+            "osk_ms_skip_off": round(off_ms, 4),
+            "stage2_osk_speedup": round(off_ms / osk_ms, 3),
+            "visited_slots": vis, "skipped_slots": skp, "causal_slots": causal,
+            "stage1_budget": round(vis / causal, 5), "skip_ratio": round(skp / max(vis, 1), 5),
+            "effective_budget": round((vis - skp) / causal, 5),
+            "osk_tflops": round(tf, 1), "osk_mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "speedup_vs_dense": None if dense_ms is None else
+            round(dense_ms / (kap_ms + osk_ms), 3),
+            "dense_baseline": None if dense_ms is None else
+            f"dense_ms of the {headline} line (same shape)"}
 
 
 def ascending_copy(bk, torch, prob, mask):

@@ -363,17 +363,3 @@ def block_mask_prefill(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor,
                                      _ptr(out.lse), _stream(dev))
     _lib.check(st, "cosa_block_mask_prefill")
     return out
-
-
-def tau_from_delta(seqlen: int, delta: float) -> float:
-    """Skip threshold in nats from the length-adaptive scale Delta.
-
-    CoSA (paperpeel) §5.1 "Hyperparameters" and App. D.1 state the threshold
-    as Delta / N with Delta = -1 disabling the skip; reading Delta / N as the
-    bound on exp(block max - running max) gives tau = ln(N / Delta).
-    """
-    if delta < 0:
-        return -1.0
-    if delta == 0:
-        raise ValueError("delta must be positive, or negative to disable the skip")
-    return math.log(seqlen / delta)

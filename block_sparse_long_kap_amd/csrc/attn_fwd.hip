@@ -629,9 +629,12 @@ __global__ __launch_bounds__(NW * HP * 64, (PPB == 1 && HP == 1) ? 2 : 1) void a
     }
 
     // ---- prefetch: K(t+NS) and V(t+NS-1) straight into LDS, and the slot
-    // chunk after the one that holds slot t+1
-    advance_chunks(t + 1);
+    // chunk after the one that holds slot t+1.  The refill of that chunk
+    // overwrites the ring half holding slot t's own entries (chunks c+1 and
+    // c-1 share a half), so it comes after the last read of slot t's pages:
+    // the on-demand V fetch below.
     if constexpr (NS == 4) {
+      advance_chunks(t + 1);
       const int tk = min(t + NS, cnt - 1);
       const int tv = min(t + NS - 1, cnt - 1);
       copy_k(tk, slot_block(tk), st);
@@ -644,8 +647,9 @@ __global__ __launch_bounds__(NW * HP * 64, (PPB == 1 && HP == 1) ? 2 : 1) void a
       if (sel && !skip && !v_have) {   // uniform over the workgroup
         copy_v(t, j_cur, st);
         wait_vm_c<0>();
-        lds_barrier();
+        lds_barrier();                 // every wave has read slot t's pages
       }
+      advance_chunks(t + 1);
       if (t + NS < cnt && selected(t + NS)) copy_k(t + NS, slot_block(t + NS), st);
       v_have = false;
       if (t + NS - 1 < cnt && selected(t + NS - 1) && !skip) {

@@ -142,6 +142,21 @@ REMAP_32K = LLAMA_32K.with_(
     budgets_sweep=(1.0, 0.3), taus_sweep=(2.0, 4.0, 6.0, 8.0),
 )
 
+# Band-only structure at 128K with the Llama shape, for the in-kernel skip.
+# With the sink and the weak stripes of llama128k no whole 128-row tile ever
+# falls tau below its running max, so the skip never fires there.  Here the
+# row maxima sit on the band blocks (about s^2 / sqrt(D) = 22.6 nats above the
+# noise) that the HRM group visits first, and the skip decides a large part
+# of the rest of each tile's walk: up to 205 visited blocks per tile at the
+# 10% budget, 615 at 30%.  (A band of s = 12 skips nothing at tau 8: the
+# random band vectors of different blocks leak about +-2.5 nats into every
+# logit, so some row of every tile stays within 8 nats of its max.)
+REMAP_128K = LLAMA_128K.with_(
+    name="remap128k", seed=7, budget=0.1, tau=8.0,
+    pattern=HeadPattern(sink=False, band=4, stripes=0, strength=16.0, q_dir=False),
+    budgets_sweep=(0.3, 0.1), taus_sweep=(2.0, 4.0, 6.0, 8.0),
+)
+
 # Test-only variant of the tiny case with a strong sink so that the in-kernel
 # skip actually fires (sink logit around 16 nats); not a benchmark workload.
 TINY_SKIP = TINY.with_(
@@ -151,7 +166,8 @@ TINY_SKIP = TINY.with_(
 )
 
 WORKLOADS: Dict[str, Workload] = {
-    w.name: w for w in (TINY, LLAMA_32K, LLAMA_128K, QWEN_128K, STRESS, REMAP_32K, TINY_SKIP)
+    w.name: w for w in (TINY, LLAMA_32K, LLAMA_128K, QWEN_128K, STRESS, REMAP_32K, REMAP_128K,
+                         TINY_SKIP)
 }
 
 

@@ -22,9 +22,9 @@
  * or frees device memory and never synchronises the host, keeps no state
  * between calls (apart from each host thread's last error message, see
  * cosa_last_error()) and enqueues all of its work on the caller's stream
- * (``stream`` is a hipStream_t; NULL is the default stream).  The caller owns every buffer.  Arguments are validated on
- * the host before any launch: an invalid call returns an error status and
- * enqueues nothing.  A launch failure returns COSA_ERR_HIP.  Only host-side
+ * (``stream`` is a hipStream_t; NULL is the default stream).  The caller
+ * owns every buffer.  Arguments are validated on the host before any
+ * launch: an invalid call returns an error status and enqueues nothing.  A launch failure returns COSA_ERR_HIP.  Only host-side
  * values are checked; device contents (page ids, sequence lengths in
  * cu_seqlens) are trusted, see cosa_check_page_table_host().
  *
@@ -42,6 +42,20 @@
  * Mask layout: "mask rows" are indexed row = (b * num_q_heads + h) * NQB + i
  * with NQB = cosa_num_q_tiles(); a mask row holds ``capacity`` int32 slots,
  * slot t at [row * capacity + t].
+ *
+ * Configurations that are valid but not built return COSA_ERR_UNSUPPORTED
+ * (before any launch):
+ *   - every entry point: head_dim other than 64 or 128; q_block other than
+ *     64 or 128; page_size other than 64; kv_block other than page_size or
+ *     2 * page_size; batch * num_q_heads * NQB above 2^31 - 1;
+ *   - the proxy entry points (cosa_proxy_ordered_mask*, and
+ *     cosa_sparse_prefill): more than 2048 logical key blocks per sequence,
+ *     ceil(max_seqlen / kv_block) > 2048, i.e. max_seqlen above 131072
+ *     tokens at kv_block 64 (262144 at kv_block 128); the attention entry
+ *     points take sequences up to max_seqlen = 2^20;
+ *   - cosa_proxy_ordered_mask_shared_kv: num_q_heads / num_kv_heads not a
+ *     power of two, or (num_q_heads / num_kv_heads) * q_block / 16 > 32;
+ *   - cosa_block_mask_prefill: kv_block != page_size.
  */
 #ifndef COSA_H_
 #define COSA_H_
@@ -150,6 +164,8 @@ cosa_status cosa_check_page_table_host(const cosa_problem* p, const int32_t* cu_
  *   debug_hrm      [rows][n_max] nullable uint8 HRM flags
  * ``capacity`` must be >= cosa_mask_capacity(p, budget).  ``workspace`` must
  * hold cosa_kap_workspace_size(p) bytes (device, any contents).
+ * COSA_ERR_UNSUPPORTED when ceil(max_seqlen / kv_block) > 2048 (the whole
+ * candidate list of a tile is scored and selected in one pass).
  */
 cosa_status cosa_proxy_ordered_mask(const cosa_problem* p, const void* q, const void* k_pool,
                                     float budget, int32_t* ordered_blocks,
@@ -255,8 +271,9 @@ cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, const void* k
  * aux_stream after the proxy of chunk c, so that the proxy of later chunks
  * overlaps it, and `stream` waits for the last kernel before the call's
  * later work; with aux_stream == NULL everything runs on `stream` in chunk
- * order.  Argument errors as for the two calls; COSA_ERR_HIP if an event
- * cannot be created.  The call allocates no device memory.
+ * order.  Argument errors (including the proxy's 2048-key-block limit) as
+ * for the two calls; COSA_ERR_HIP if an event cannot be created.  The call
+ * allocates no device memory.
  */
 cosa_status cosa_sparse_prefill(const cosa_problem* p, const void* q, const void* k_pool,
                                 const void* v_pool, float budget, float skip_tau,

@@ -2,12 +2,12 @@
 
 Usage (after the rocprofv3 runs named in each mode's docstring)::
 
-    python -m block_sparse_long_kap_amd.profsum stats    KERNEL_STATS.csv  --command "..."
-    python -m block_sparse_long_kap_amd.profsum trace    KERNEL_TRACE.csv  --command "..."
-    python -m block_sparse_long_kap_amd.profsum traffic  FETCH.csv WRITE.csv COPY_FETCH.csv \
+    python3 profsum.py stats    KERNEL_STATS.csv  --command "..."
+    python3 profsum.py trace    KERNEL_TRACE.csv  --command "..."
+    python3 profsum.py traffic  FETCH.csv WRITE.csv COPY_FETCH.csv \
         COPY_WRITE.csv --copy-bytes 1073741824 --workload llama128k --budget 0.1 --tau 8 \
         --command "..."
-    python -m block_sparse_long_kap_amd.profsum counters COUNTERS.csv --command "..."
+    python3 profsum.py counters COUNTERS.csv --command "..."
 
 Each mode prints Markdown.  The traffic mode also prints one
 ``bench-traffic: {json}`` line per attention kernel, which ``bench.py`` reads
@@ -26,7 +26,8 @@ import os
 import re
 import sys
 
-PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+# measurement tooling beside bench.py, not part of the library
+PKG_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_sparse_long_kap_amd")
 ATTN_SOURCES = ("csrc/attn_fwd.hip", "csrc/cosa_internal.h", "csrc/cosa_api.hip")
 
 

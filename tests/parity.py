@@ -26,6 +26,36 @@ MARGIN_TOL = 1e-3
 W_RTOL = 1e-4
 HRM_GAP = 1e-4
 
+# One line per parity check with its tallies (exact rows, near-ties,
+# near-threshold slots ...), printed again in the terminal summary by
+# tests/conftest.py so that a quiet run still shows them.
+SUMMARY: list = []
+
+
+def report(label: str, **counts) -> None:
+    line = f"{label}: " + " ".join(f"{k}={v}" for k, v in counts.items())
+    SUMMARY.append(line)
+    print(f"[parity] {line}", flush=True)
+
+
+def selection_on_own_scores(w32, hrm, n, beta_ppm, top_p=1.0):
+    """The documented selection rule applied to a kernel's own exported fp32
+    importance scores and HRM flags: HRM-first order (w descending, block
+    ascending inside each group), budget count, and with top_p < 1 the Top-p
+    count over w rounded down to 2^-48 (p likewise).  The kernel's mask must
+    equal this bit for bit."""
+    from oracle import kap as okap
+    w32 = np.asarray(w32[:n], dtype=np.float32)
+    order = okap.flag_grouped_order(w32.astype(np.float64), np.asarray(hrm[:n], dtype=bool))
+    k = okap.budget_count(n, beta_ppm)
+    if top_p < 1.0:
+        fx = np.floor(w32.astype(np.float64) * 2.0 ** 48).astype(np.int64)
+        target = int(np.floor(np.float64(np.float32(top_p)) * 2.0 ** 48))
+        cum = np.cumsum(fx[order])
+        hit = np.flatnonzero(cum >= target)
+        k = min(k, int(hit[0]) + 1 if hit.size else n)
+    return order[:k]
+
 
 def upload(x, device, q_block=None):
     """Seeded inputs (bf16-rounded float32 numpy) -> device tensors + Problem."""

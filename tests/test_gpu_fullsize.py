@@ -17,7 +17,8 @@ from oracle import kap as okap
 from oracle import osk as oosk
 from oracle.paging import materialise
 
-from .parity import ErrStats, check_kap_row, check_osk_tile, upload
+from .parity import (MAX_ABS, MEAN_ABS, ErrStats, check_kap_row, check_osk_tile, report,
+                     selection_on_own_scores, upload)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -51,7 +52,9 @@ def test_full_layer_sampled_parity(name, n_samples):
     x = ci.make(w).bf16_rounded()
     prob, q, k, v = upload(x, DEV)
     print(f"[case] full-size {name}: GPU layer", flush=True)
-    m = bk.proxy_ordered_mask(prob, q, k, w.budget)
+    # the proxy instance bench.py times (the score export is a runtime option
+    # of the same kernel)
+    m = bk.proxy_ordered_mask(prob, q, k, w.budget, debug=True)
     r = bk.osk_prefill(prob, q, k, v, m, w.tau)
     torch.cuda.synchronize()
     # the fused call at full size, the kernel on a second stream: same bits
@@ -66,6 +69,7 @@ def test_full_layer_sampled_parity(name, n_samples):
     assert torch.equal(fr.row_stats, r.row_stats)
     del fm, fr
     gb, gp, gc, gh = _np(m.blocks), _np(m.pages), _np(m.counts), _np(m.hrm_counts)
+    dw, dh = _np(m.debug_w), _np(m.debug_hrm)
     out, lse, rec, stats = _np(r.out), _np(r.lse), _np(r.skip_record), _np(r.row_stats)
     del r
     d = bk.dense_prefill(prob, q, k, v)
@@ -86,13 +90,27 @@ def test_full_layer_sampled_parity(name, n_samples):
         assert np.array_equal(gp[b][sel], x.page_table[b][gb[b][sel]])
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(dout))
     assert np.array_equal(stats[..., 0], gc)
+    # bit-exact: the selection rule on the kernel's own scores, on a seeded
+    # sample of mask rows (plus every row the oracle checks below)
+    picks = _sample(w, x, n_samples, seed=w.seed)
+    rng = np.random.default_rng(w.seed + 100)
+    own_rows = set(picks)
+    for _ in range(512):
+        b = int(rng.integers(w.batch))
+        own_rows.add((b, int(rng.integers(w.num_q_heads)),
+                      int(rng.integers((int(lens[b]) + w.q_block - 1) // w.q_block))))
+    for (b, h, i) in sorted(own_rows):
+        n = (min((i + 1) * w.q_block, int(lens[b])) - 1) // w.page_size + 1
+        want = selection_on_own_scores(dw[b, h, i], dh[b, h, i], n, beta)
+        c = int(gc[b, h, i])
+        assert c == len(want) and np.array_equal(gb[b, h, i, :c], want), (b, h, i)
+    del dw, dh
     # sampled oracle checks
     grp = w.num_q_heads // w.num_kv_heads
     kap_exact = kap_tie = 0
     so, sl, do, dl = ErrStats(), ErrStats(), ErrStats(), ErrStats()
     near = 0
     cache = {}
-    picks = _sample(w, x, n_samples, seed=w.seed)
     print(f"[case] full-size {name}: oracle on {len(picks)} tiles", flush=True)
     for (b, h, i) in picks:
         s0, L = int(x.cu_seqlens[b]), int(lens[b])
@@ -119,8 +137,9 @@ def test_full_layer_sampled_parity(name, n_samples):
         o, ls = odense.attention_rows(qr, rows, kk[:, g], vv[:, g], w.softmax_scale)
         do.add(dout[s0 + rows, h], o)
         dl.add(dlse[h, s0 + rows], ls)
-    print(f"[parity] {name}: KAP exact={kap_exact} near-tie={kap_tie}; OSK near-threshold "
-          f"slots={near}; layer skipped={int(stats[..., 1].sum())} of {int(stats[..., 0].sum())}")
+    report(f"full-size {name}", own_score_exact=len(own_rows), kap_exact=kap_exact,
+           kap_near_tie=kap_tie, osk_near_threshold=near,
+           layer_skipped=int(stats[..., 1].sum()), layer_visited=int(stats[..., 0].sum()))
     so.assert_ok(label=f"{name} osk out")
     sl.assert_ok(max_abs=1e-3, mean_abs=1e-4, label=f"{name} osk lse")
     do.assert_ok(label=f"{name} dense out")
@@ -168,8 +187,177 @@ def test_full_layer_shared_kv_sampled_parity():
                                             w.softmax_scale, w.page_size)
             near += check_osk_tile(out[rows, h], lse[h, rows], rec[0, h, i], res, qr, rows,
                                    kk[:, g], vv[:, g], bl, w.softmax_scale, w.page_size, so, sl)
-    print(f"[parity] shared-kv llama128k: KAP rows exact={exact} of {len(picks)}; "
-          f"near-threshold slots={near}")
+    report("full-size shared-kv llama128k", kap_exact=exact, kap_rows=len(picks),
+           osk_near_threshold=near)
     so.assert_ok(label="shared-kv osk out")
     sl.assert_ok(max_abs=1e-3, mean_abs=1e-4, label="shared-kv osk lse")
     assert exact >= len(picks) // 2
+
+
+# ---------------------------------------------------------------------------
+# The in-kernel skip on long tiles.  The kernel reads each tile's slot
+# lookups from a ring of two 64-slot chunks in LDS and refills a chunk from
+# memory every 64 slots; tiles with more than 128 visited blocks take that
+# refill, and a computed block right after a skipped one fetches its V page
+# on demand.  These cases make the skip fire on such tiles at full size.
+
+
+def _refill_after_skip(gc, rec):
+    """Mask rows (b, h, i) with a slot 64c - 1 (c >= 1) that is computed right
+    after a skipped slot while a later chunk of the ring is still refilled
+    (64 (c + 1) < count)."""
+    hit = np.zeros(gc.shape, dtype=bool)
+    C = rec.shape[-1]
+    for c in range(1, C // 64 + 1):
+        t = 64 * c - 1
+        if t >= C:
+            break
+        hit |= (gc > 64 * (c + 1)) & (rec[..., t - 1] == 1) & (rec[..., t] == 0)
+    return hit
+
+
+def _long_tile_picks(w, gc, rec, stats, seed):
+    rng = np.random.default_rng(seed)
+    B, H, _ = gc.shape
+    picks = set()
+    # the longest tile of four heads of every sequence
+    for b in range(B):
+        i_long = int(np.argmax(gc[b, 0]))
+        for h in (0, H // 3, 2 * H // 3, H - 1):
+            picks.add((b, h, i_long))
+    # rows that cross a ring refill right after a skipped block
+    trig = np.argwhere(_refill_after_skip(gc, rec))
+    for r in rng.permutation(len(trig))[:6]:
+        picks.add(tuple(int(v) for v in trig[r]))
+    # long rows on which the skip fired
+    long_skip = np.argwhere((gc > 128) & (stats[..., 1] > 0))
+    for r in rng.permutation(len(long_skip))[:6]:
+        picks.add(tuple(int(v) for v in long_skip[r]))
+    # any rows
+    live = np.argwhere(gc > 0)
+    for r in rng.permutation(len(live))[:4]:
+        picks.add(tuple(int(v) for v in live[r]))
+    return sorted(picks), len(trig), len(long_skip)
+
+
+LONG_SKIP_CASES = [
+    ("remap32k", {}, 1.0, 2.0),
+    ("remap32k", {}, 1.0, 6.0),
+    ("remap32k", {}, 0.3, 2.0),
+    ("remap32k", {}, 0.3, 6.0),
+    ("remap32k", {"kv_block": 128}, 1.0, 4.0),
+    ("remap128k", {}, 0.1, 8.0),
+]
+
+
+@pytest.mark.parametrize("case", LONG_SKIP_CASES,
+                         ids=[f"{n}{'-kv128' if kw else ''}-b{b}-t{t}"
+                              for n, kw, b, t in LONG_SKIP_CASES])
+def test_long_tile_skip_parity(case):
+    name, kw, budget, tau = case
+    w = ci.get(name).with_(**kw) if kw else ci.get(name)
+    print(f"[case] long-tile skip {name} {kw} budget={budget} tau={tau}: inputs", flush=True)
+    x = ci.make(w).bf16_rounded()
+    prob, q, k, v = upload(x, DEV)
+    print(f"[case] long-tile skip {name} {kw} budget={budget} tau={tau}: GPU layer", flush=True)
+    m = bk.proxy_ordered_mask(prob, q, k, budget)
+    r = bk.osk_prefill(prob, q, k, v, m, tau)
+    torch.cuda.synchronize()
+    gb, gc = _np(m.blocks), _np(m.counts)
+    out, lse, rec, stats = _np(r.out), _np(r.lse), _np(r.skip_record), _np(r.row_stats)
+    del m, r, q, k, v
+    assert np.all(np.isfinite(out))
+    assert np.array_equal(stats[..., 0], gc)
+    long_rows = gc > 128
+    assert long_rows.any(), "no tile visits more than 128 blocks"
+    assert int(stats[..., 1][long_rows].sum()) > 0, "the skip never fires on a long tile"
+    picks, n_trig, n_long_skip = _long_tile_picks(w, gc, rec, stats, seed=w.seed + 7)
+    lens = np.diff(x.cu_seqlens)
+    grp = w.num_q_heads // w.num_kv_heads
+    so, sl = ErrStats(), ErrStats()
+    near = skipped = slots = 0
+    cache = {}
+    print(f"[case] long-tile skip {name}: oracle on {len(picks)} tiles", flush=True)
+    for (b, h, i) in picks:
+        s0, L = int(x.cu_seqlens[b]), int(lens[b])
+        if b not in cache:
+            cache = {b: (materialise(x.k_pool, x.page_table[b], L, w.page_size),
+                         materialise(x.v_pool, x.page_table[b], L, w.page_size))}
+        kk, vv = cache[b]
+        g = h // grp
+        rows = np.arange(i * w.q_block, min((i + 1) * w.q_block, L))
+        qr = x.q[s0 + rows, h].astype(np.float64)
+        cnt = int(gc[b, h, i])
+        bl = gb[b, h, i, :cnt]
+        res = oosk.osk_tile_closed_form(qr, rows, kk[:, g], vv[:, g], bl, tau,
+                                        w.softmax_scale, w.block)
+        near += check_osk_tile(out[s0 + rows, h], lse[h, s0 + rows], rec[b, h, i], res, qr,
+                               rows, kk[:, g], vv[:, g], bl, w.softmax_scale, w.block, so, sl)
+        assert stats[b, h, i, 1] == int(rec[b, h, i, :cnt].sum())
+        skipped += int(rec[b, h, i, :cnt].sum())
+        slots += cnt
+    report(f"long-tile skip {name}{'-kv128' if kw else ''} b={budget} tau={tau}",
+           tiles=len(picks), longest=int(gc.max()), refill_after_skip_rows=n_trig,
+           long_rows_with_skips=n_long_skip, sampled_skipped=skipped, sampled_slots=slots,
+           osk_near_threshold=near, layer_skip_ratio=round(
+               float(stats[..., 1].sum()) / max(float(stats[..., 0].sum()), 1.0), 4))
+    so.assert_ok(label=f"long-tile {name} osk out")
+    sl.assert_ok(max_abs=1e-3, mean_abs=1e-4, label=f"long-tile {name} osk lse")
+
+
+def test_stress_full_budget_skip_off_equals_dense():
+    """The stress batch (16K + 48K + 96K + 128K in one pool) at a 100% stage-1
+    budget with the in-kernel skip off (tau < 0, Delta = -1 of App. D.1): the
+    OSK visits every causal block in the proxy's order and must give dense
+    attention; compared with the dense kernel on every row and with the
+    oracle on sampled tiles."""
+    w = ci.get("stress")
+    print("[case] stress beta=1 skip off: inputs", flush=True)
+    x = ci.make(w).bf16_rounded()
+    prob, q, k, v = upload(x, DEV)
+    print("[case] stress beta=1 skip off: GPU layer", flush=True)
+    m = bk.proxy_ordered_mask(prob, q, k, 1.0)
+    r = bk.osk_prefill(prob, q, k, v, m, -1.0)
+    d = bk.dense_prefill(prob, q, k, v)
+    torch.cuda.synchronize()
+    gc, stats = _np(m.counts), _np(r.row_stats)
+    lens = np.diff(x.cu_seqlens)
+    for b in range(w.batch):
+        nqb = (int(lens[b]) + w.q_block - 1) // w.q_block
+        n_i = (np.minimum((np.arange(nqb) + 1) * w.q_block, lens[b]) - 1) // w.page_size + 1
+        assert np.all(gc[b, :, :nqb] == n_i[None, :])
+    assert int(stats[..., 1].sum()) == 0
+    # every row: OSK against the dense kernel (a different visiting order),
+    # reduced on the device (1.2e9 elements).  Each of the two bf16 results is
+    # held to MAX_ABS / MEAN_ABS of the exact value (the sampled oracle check
+    # below, and the dense kernel's own parity tests), so their difference is
+    # bounded by twice that; one bf16 ulp of an output in [4, 8) is already
+    # 2^-5.
+    diff = (r.out.float() - d.out.float()).abs()
+    assert bool(torch.isfinite(diff).all())
+    mx, mean = float(diff.max()), float(diff.double().mean())
+    del diff
+    print(f"[parity] stress beta=1 osk vs dense kernel: max_abs={mx:.3e} mean_abs={mean:.3e}")
+    assert mx <= 2 * MAX_ABS and mean <= 2 * MEAN_ABS, (mx, mean)
+    out, lse = _np(r.out), _np(r.lse)
+    del m, r, d, q, k, v
+    picks = _sample(w, x, 10, seed=w.seed + 3)
+    grp = w.num_q_heads // w.num_kv_heads
+    so, sl = ErrStats(), ErrStats()
+    cache = {}
+    for (b, h, i) in picks:
+        s0, L = int(x.cu_seqlens[b]), int(lens[b])
+        if b not in cache:
+            cache = {b: (materialise(x.k_pool, x.page_table[b], L, w.page_size),
+                         materialise(x.v_pool, x.page_table[b], L, w.page_size))}
+        kk, vv = cache[b]
+        rows = np.arange(i * w.q_block, min((i + 1) * w.q_block, L))
+        o, ls = odense.attention_rows(x.q[s0 + rows, h].astype(np.float64), rows,
+                                      kk[:, h // grp], vv[:, h // grp], w.softmax_scale)
+        so.add(out[s0 + rows, h], o)
+        sl.add(lse[h, s0 + rows], ls)
+    report("stress beta=1 skip off vs dense", tiles=len(picks),
+           visited=int(stats[..., 0].sum()), kernel_max_abs=f"{mx:.2e}",
+           kernel_mean_abs=f"{mean:.2e}")
+    so.assert_ok(label="stress beta=1 osk vs oracle dense")
+    sl.assert_ok(max_abs=1e-3, mean_abs=1e-4, label="stress beta=1 osk lse")

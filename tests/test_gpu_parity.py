@@ -18,7 +18,8 @@ from oracle import kap as okap
 from oracle import osk as oosk
 from oracle.paging import materialise
 
-from .parity import ErrStats, check_kap_row, check_osk_tile, expected_pages, upload
+from .parity import (ErrStats, check_kap_row, check_osk_tile, expected_pages, report,
+                     selection_on_own_scores, upload)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -147,7 +148,7 @@ def _run_osk_vs_oracle(w, x, blocks, counts, tau, label, tiles=None, delta=None,
                 n_skipped += int(rec[b, h, i, :cnt].sum())
                 assert stats[b, h, i, 0] == cnt
                 assert stats[b, h, i, 1] == int(rec[b, h, i, :cnt].sum())
-    print(f"[parity] {label}: in-kernel skipped slots={n_skipped} near-threshold={near_total}")
+    report(label, skipped=n_skipped, near_threshold=near_total)
     st.assert_ok(label=f"{label} out")
     ls.assert_ok(max_abs=1e-3, mean_abs=1e-4, label=f"{label} lse")
     return n_skipped
@@ -199,9 +200,11 @@ def _kap_compare(w, x, budget, label, tiles=None, debug=True):
     gm = bk.proxy_ordered_mask(prob, q, k, budget, debug=debug)
     torch.cuda.synchronize()
     gb, gp, gc, gh = _np(gm.blocks), _np(gm.pages), _np(gm.counts), _np(gm.hrm_counts)
+    dw = _np(gm.debug_w) if debug else None
+    dh = _np(gm.debug_hrm) if debug else None
     beta = okap.budget_ppm(budget)
     assert gm.capacity == okap.mask_capacity(int(max(w.seqlens)), w.block, beta)
-    exact = ties = 0
+    exact = ties = own = 0
     grp = w.num_q_heads // w.num_kv_heads
     for b in range(w.batch):
         s0, L = int(x.cu_seqlens[b]), int(x.seqlens[b])
@@ -218,12 +221,18 @@ def _kap_compare(w, x, budget, label, tiles=None, debug=True):
             res = okap.head_tiles(x.q[s0:s0 + L, h].astype(np.float64), kk[:, h // grp],
                                   w.softmax_scale, w.q_block, w.block, beta, tiles=want)
             for i, tile in res.items():
+                if debug:
+                    # bit-exact: the selection rule on the kernel's own w and flags
+                    want = selection_on_own_scores(dw[b, h, i], dh[b, h, i], tile.n, beta)
+                    c = int(gc[b, h, i])
+                    assert c == len(want) and np.array_equal(gb[b, h, i, :c], want), (b, h, i)
+                    own += 1
                 kind = check_kap_row(gb[b, h, i], gp[b, h, i], gc[b, h, i], gh[b, h, i], tile,
                                      x.page_table[b], ppb=w.block // w.page_size,
                                      kv_block=w.block, L=L)
                 exact += kind == "exact"
                 ties += kind == "tie"
-    print(f"[parity] {label}: KAP rows exact={exact} near-tie={ties}")
+    report(label, own_score_exact=own, exact=exact, near_tie=ties)
     return gm, exact, ties
 
 
@@ -286,21 +295,6 @@ def test_osk_delta_per_sequence_threshold(delta):
 TOP_P_TOL = 1e-5   # fp32 importance scores against fp64: mass near-ties
 
 
-def _fixed_point_selection(w32, hrm, n, beta_ppm, top_p):
-    """The documented selection applied to the GPU's own fp32 w and HRM flags:
-    HRM-first order, budget count, Top-p count over w rounded down to 2^-48."""
-    w32 = np.asarray(w32[:n], dtype=np.float32)
-    order = okap.flag_grouped_order(w32.astype(np.float64), np.asarray(hrm[:n], dtype=bool))
-    k = okap.budget_count(n, beta_ppm)
-    if top_p < 1.0:
-        fx = np.floor(w32.astype(np.float64) * 2.0 ** 48).astype(np.int64)
-        target = int(np.floor(np.float64(np.float32(top_p)) * 2.0 ** 48))
-        cum = np.cumsum(fx[order])
-        hit = np.flatnonzero(cum >= target)
-        k = min(k, int(hit[0]) + 1 if hit.size else n)
-    return order[:k]
-
-
 def _allowed_counts(tile, top_p, beta_ppm):
     kb = okap.budget_count(tile.n, beta_ppm)
     if top_p >= 1.0:
@@ -342,7 +336,7 @@ def test_kap_top_p_matches_oracle(case):
             for i, tile in res.items():
                 c = int(gc[b, h, i])
                 # 1) bit-exact: the documented rule on the kernel's own w and flags
-                want = _fixed_point_selection(dw[b, h, i], dh[b, h, i], tile.n, beta, top_p)
+                want = selection_on_own_scores(dw[b, h, i], dh[b, h, i], tile.n, beta, top_p)
                 assert c == len(want) and np.array_equal(gb[b, h, i, :c], want), (b, h, i)
                 # 2) against the fp64 oracle: the count up to mass near-ties,
                 #    then the kept blocks as for the budget mask
@@ -352,8 +346,8 @@ def test_kap_top_p_matches_oracle(case):
                                      dataclasses.replace(tile, k=c), x.page_table[b])
                 exact += kind == "exact" and c == tile.k
                 ties += kind == "tie" or c != tile.k
-    print(f"[parity] kap top_p={top_p} cap={cap}: rows exact={exact} near-tie={ties} "
-          f"truncated={shorter}")
+    report(f"kap top_p={top_p} cap={cap}", own_score_exact=exact + ties, exact=exact,
+           near_tie=ties, truncated=shorter)
     assert exact > 0 and ties <= max(1, exact // 100)
     if top_p < 1.0:
         assert shorter > 0
@@ -455,7 +449,7 @@ def test_kap_shared_kv_matches_oracle(case):
                                    top_p=tp)
             for i, tile in res.items():
                 c = int(gc[b, g, i])
-                want = _fixed_point_selection(dw[b, g, i], dh[b, g, i], tile.n, beta,
+                want = selection_on_own_scores(dw[b, g, i], dh[b, g, i], tile.n, beta,
                                               1.0 if tp is None else tp)
                 assert c == len(want) and np.array_equal(gb[b, g, i, :c], want), (b, g, i)
                 if tp is not None:
@@ -464,7 +458,7 @@ def test_kap_shared_kv_matches_oracle(case):
                                      dataclasses.replace(tile, k=c), x.page_table[b])
                 exact += kind == "exact" and c == tile.k
                 ties += kind == "tie" or c != tile.k
-    print(f"[parity] kap shared {name}: rows exact={exact} near-tie={ties}")
+    report(f"kap shared {name}", exact=exact, near_tie=ties)
     assert exact > 0 and ties <= max(1, exact // 100)
 
 

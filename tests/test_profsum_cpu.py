@@ -2,7 +2,7 @@
 import csv
 import os
 
-from block_sparse_long_kap_amd import profsum
+import profsum
 
 
 def test_digest_ignores_comments_only():
