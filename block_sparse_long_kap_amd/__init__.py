@@ -8,5 +8,6 @@ not been built (``python -m block_sparse_long_kap_amd.build``).
 from .api import (KapWorkspace, OrderedMask, PrefillOutput, Problem,  # noqa: F401
                   block_mask_prefill, dense_prefill, osk_prefill, osk_prefill_delta,
                   osk_prefill_shared_kv,
-                  proxy_ordered_mask, proxy_ordered_mask_shared_kv, proxy_ordered_mask_top_p,
+                  proxy_ordered_mask, proxy_ordered_mask_no_alloc,
+                  proxy_ordered_mask_shared_kv, proxy_ordered_mask_top_p,
                   sparse_prefill)

@@ -21,6 +21,8 @@ COSA_ERR_INVALID_ARG = -1
 COSA_ERR_UNSUPPORTED = -2
 COSA_ERR_WORKSPACE = -3
 COSA_ERR_HIP = -4
+# bytes of the static workspace of cosa_proxy_ordered_mask_no_alloc
+NO_ALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class CosaProblem(ctypes.Structure):
@@ -58,6 +60,8 @@ SIGNATURES = {
                                         c_i64, c_vp, c_size, c_vp]),
     "cosa_proxy_ordered_mask_top_p": (c_i32, [P, c_vp, c_vp, c_f32, c_f32, c_vp, c_vp, c_vp,
                                               c_vp, c_vp, c_vp, c_i64, c_vp, c_size, c_vp]),
+    "cosa_proxy_ordered_mask_no_alloc": (c_i32, [P, c_vp, c_vp, c_f32, c_vp, c_vp, c_vp, c_vp,
+                                                c_vp, c_vp, c_i64, c_vp]),
     "cosa_proxy_ordered_mask_shared_kv": (c_i32, [P, c_vp, c_vp, c_f32, c_f32, c_vp, c_vp,
                                                  c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_size,
                                                  c_vp]),

@@ -184,6 +184,23 @@ def proxy_ordered_mask(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor, 
     return out
 
 
+def proxy_ordered_mask_no_alloc(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor,
+                                budget: float, *, capacity: Optional[int] = None,
+                                hrm_counts: bool = True, debug: bool = False,
+                                out: Optional[OrderedMask] = None) -> OrderedMask:
+    """KAP ordered mask with the library's static workspace
+    (``cosa_proxy_ordered_mask_no_alloc``): pass ``out`` to allocate nothing
+    on this side either."""
+    lib = _lib.load()
+    out = _mask_buffers(problem, q, k_pool, budget, capacity, hrm_counts, debug, out)
+    st = lib.cosa_proxy_ordered_mask_no_alloc(
+        problem.ref(), _ptr(q), _ptr(k_pool), ctypes.c_float(budget), _ptr(out.blocks),
+        _ptr(out.pages), _ptr(out.counts), _ptr(out.hrm_counts), _ptr(out.debug_w),
+        _ptr(out.debug_hrm), out.capacity, _stream(problem.device))
+    _lib.check(st, "cosa_proxy_ordered_mask_no_alloc")
+    return out
+
+
 def proxy_ordered_mask_top_p(problem: Problem, q: torch.Tensor, k_pool: torch.Tensor,
                              top_p: float, budget: float = 1.0, *,
                              capacity: Optional[int] = None, hrm_counts: bool = True,

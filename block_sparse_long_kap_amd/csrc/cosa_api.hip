@@ -1,10 +1,14 @@
 // Host side of the C ABI declared in include/cosa.h: argument validation,
-// sizing and kernel launches.  No allocation, no synchronisation, no state
-// between calls other than a thread-local text for the last error.
+// sizing and kernel launches.  No allocation and no synchronisation; the
+// state kept between calls is a thread-local text for the last error and,
+// per device, the address of the static workspace of the no-allocation
+// proxy entry point.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+
+#include <mutex>
 
 #include "cosa.h"
 #include "cosa_internal.h"
@@ -193,12 +197,13 @@ COSA_EXPORT cosa_status cosa_check_page_table_host(const cosa_problem* p,
 
 namespace {
 
-// Validates the proxy's arguments and fills its kernel parameters.
+// Validates the proxy's arguments and fills its kernel parameters
+// (check_workspace false: the caller supplies the workspace afterwards).
 cosa_status build_kap(cosa::KapParams& k, const cosa_problem* p, const void* q, const void* k_pool,
                       float budget, uint64_t top_p_fx, bool shared, int32_t* ordered_blocks,
                       int32_t* ordered_pages, int32_t* counts, int32_t* hrm_counts, float* debug_w,
                       uint8_t* debug_hrm, int64_t capacity, void* workspace,
-                      size_t workspace_bytes) {
+                      size_t workspace_bytes, bool check_workspace = true) {
   cosa_status st = validate(p);
   if (st != COSA_OK) return st;
   if (q == nullptr || k_pool == nullptr || ordered_blocks == nullptr ||
@@ -212,7 +217,7 @@ cosa_status build_kap(cosa::KapParams& k, const cosa_problem* p, const void* q, 
   if (capacity < budget_count(n_max, ppm))
     return fail(COSA_ERR_INVALID_ARG, "capacity < cosa_mask_capacity(problem, budget)");
   const size_t need = cosa_kap_workspace_size(p);
-  if (workspace == nullptr || workspace_bytes < need)
+  if (check_workspace && (workspace == nullptr || workspace_bytes < need))
     return fail(COSA_ERR_WORKSPACE, "workspace null or smaller than cosa_kap_workspace_size()");
   k.q = static_cast<const uint16_t*>(q);
   k.k_pool = static_cast<const uint16_t*>(k_pool);
@@ -276,6 +281,69 @@ COSA_EXPORT cosa_status cosa_proxy_ordered_mask(const cosa_problem* p, const voi
                                                 size_t workspace_bytes, void* stream) {
   return proxy_mask(p, q, k_pool, budget, 0, false, ordered_blocks, ordered_pages, counts,
                     hrm_counts, debug_w, debug_hrm, capacity, workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+// Workspace of cosa_proxy_ordered_mask_no_alloc(), for callers that cannot
+// allocate device memory: a file-scope device array, one copy per GPU the
+// library runs on, held until the process ends.  On the host its name is a
+// stand-in, not a device address: host code only ever uses the address that
+// hipGetSymbolAddress returns for the device, looked up once per device on
+// its first call.
+static __device__ __align__(256) unsigned char scratch[COSA_NO_ALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device that runs `stream` (the
+// current device for the null stream).
+cosa_status scratch_address(hipStream_t stream, void** addr) {
+  int dev = -1;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(COSA_ERR_HIP, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(COSA_ERR_UNSUPPORTED, "device ordinal beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return fail(COSA_ERR_HIP, hipGetErrorString(e));
+    if (ptr == nullptr) return fail(COSA_ERR_HIP, "hipGetSymbolAddress returned null");
+    g_scratch_addr[dev] = ptr;
+  }
+  *addr = g_scratch_addr[dev];
+  return COSA_OK;
+}
+
+}  // namespace
+
+COSA_EXPORT cosa_status cosa_proxy_ordered_mask_no_alloc(
+    const cosa_problem* p, const void* q, const void* k_pool, float budget,
+    int32_t* ordered_blocks, int32_t* ordered_pages, int32_t* counts, int32_t* hrm_counts,
+    float* debug_w, uint8_t* debug_hrm, int64_t capacity, void* stream) {
+  cosa::KapParams k;
+  cosa_status st = build_kap(k, p, q, k_pool, budget, 0, false, ordered_blocks, ordered_pages,
+                             counts, hrm_counts, debug_w, debug_hrm, capacity, nullptr, 0,
+                             /*check_workspace=*/false);
+  if (st != COSA_OK) return st;
+  if (cosa_kap_workspace_size(p) > (size_t)COSA_NO_ALLOC_SCRATCH_BYTES)
+    return fail(COSA_ERR_WORKSPACE,
+                "the problem needs more than COSA_NO_ALLOC_SCRATCH_BYTES of workspace "
+                "(cosa_kap_workspace_size); use cosa_proxy_ordered_mask with a workspace");
+  void* ws = nullptr;
+  st = scratch_address((hipStream_t)stream, &ws);
+  if (st != COSA_OK) return st;
+  k.kbar = static_cast<uint16_t*>(ws);
+  return hip_status(cosa::launch_kap(k, p->head_dim, p->q_block, (hipStream_t)stream));
 }
 
 COSA_EXPORT cosa_status cosa_proxy_ordered_mask_shared_kv(

@@ -21,7 +21,9 @@
  * Pointers named "device" point to GPU memory; the library never allocates
  * or frees device memory and never synchronises the host, keeps no state
  * between calls (apart from each host thread's last error message, see
- * cosa_last_error()) and enqueues all of its work on the caller's stream
+ * cosa_last_error(), and the static workspace of
+ * cosa_proxy_ordered_mask_no_alloc()) and enqueues all of its work on the
+ * caller's stream
  * (``stream`` is a hipStream_t; NULL is the default stream).  The caller
  * owns every buffer.  Arguments are validated on the host before any
  * launch: an invalid call returns an error status and enqueues nothing.  A launch failure returns COSA_ERR_HIP.  Only host-side
@@ -173,6 +175,33 @@ cosa_status cosa_proxy_ordered_mask(const cosa_problem* p, const void* q, const 
                                     int32_t* hrm_counts, float* debug_w, uint8_t* debug_hrm,
                                     int64_t capacity, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and outputs as cosa_proxy_ordered_mask(), bit for bit, with
+ * the pooled-key workspace held in a static device array of the library
+ * instead of a caller's buffer.  Every GPU the library runs on holds its own
+ * COSA_NO_ALLOC_SCRATCH_BYTES copy until the process ends; its device
+ * address is looked up once per device (hipGetSymbolAddress) on the first
+ * call there.  The call allocates nothing, device or host.
+ *
+ * Limit: problems with cosa_kap_workspace_size(p) >
+ * COSA_NO_ALLOC_SCRATCH_BYTES (32 MiB: four 128K sequences with 8 KV heads
+ * of head_dim 128) return COSA_ERR_WORKSPACE before any launch.  The array
+ * keeps the last call's contents between calls and every call on a GPU uses
+ * the same array, so calls that overlap on one GPU (on different streams)
+ * race; a call needs no zeroed array (the proxy writes every pooled key it
+ * reads).  Other arguments and errors as for cosa_proxy_ordered_mask();
+ * COSA_ERR_HIP if the stream's device cannot be queried.
+ */
+#define COSA_NO_ALLOC_SCRATCH_BYTES (32u << 20)
+cosa_status cosa_proxy_ordered_mask_no_alloc(const cosa_problem* p, const void* q,
+                                             const void* k_pool, float budget,
+                                             int32_t* ordered_blocks, int32_t* ordered_pages,
+                                             int32_t* counts, int32_t* hrm_counts,
+                                             float* debug_w, uint8_t* debug_hrm,
+                                             int64_t capacity, void* stream);
 
 /*
  * Kernel-Aware Proxy with stage-1 Top-p (CoSA (paperpeel) §5.1

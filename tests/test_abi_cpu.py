@@ -182,3 +182,29 @@ def test_host_page_table_check(lib):
     cu_bad = np.array([0, 200, 331], dtype=np.int32)
     assert lib.cosa_check_page_table_host(ctypes.byref(p), vp(cu_bad), vp(pt)) == -1
     assert lib.cosa_check_page_table_host(ctypes.byref(p), None, vp(pt)) == -1
+
+
+def test_no_alloc_proxy_rejects_before_any_hip_call(lib):
+    """cosa_proxy_ordered_mask_no_alloc checks its arguments and the size of
+    the static workspace on the host, before it looks up the device."""
+    p = _problem()
+    pr = ctypes.byref(p)
+    cap = lib.cosa_mask_capacity(pr, 0.1)
+    E = _lib.COSA_ERR_INVALID_ARG
+    assert lib.cosa_proxy_ordered_mask_no_alloc(pr, None, 1, 0.1, 1, 1, 1, None, None, None,
+                                                cap, None) == E
+    assert lib.cosa_proxy_ordered_mask_no_alloc(pr, 1, 1, 0.1, 1, 1, 1, None, None, None,
+                                                cap - 1, None) == E
+    assert lib.cosa_proxy_ordered_mask_no_alloc(pr, 1, 1, 1.5, 1, 1, 1, None, None, None,
+                                                cap, None) == E
+    # four 128K sequences with 8 KV heads fit the 32 MiB array exactly, five do not
+    fits = _problem(batch=4, total_q=4 * 131072)
+    assert lib.cosa_kap_workspace_size(ctypes.byref(fits)) == _lib.NO_ALLOC_SCRATCH_BYTES
+    big = _problem(batch=5, total_q=5 * 131072)
+    assert lib.cosa_kap_workspace_size(ctypes.byref(big)) > _lib.NO_ALLOC_SCRATCH_BYTES
+    assert lib.cosa_proxy_ordered_mask_no_alloc(ctypes.byref(big), 1, 1, 0.1, 1, 1, 1, None,
+                                                None, None, cap, None) == \
+        _lib.COSA_ERR_WORKSPACE
+    assert "COSA_NO_ALLOC_SCRATCH_BYTES" in lib.cosa_last_error().decode()
+    # the header states the same size
+    assert re.search(r"#define COSA_NO_ALLOC_SCRATCH_BYTES \(32u << 20\)", open(HEADER).read())
