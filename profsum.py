@@ -117,11 +117,14 @@ def trace_md(path, command):
                int(r["Grid_Size_Z"]) // max(1, int(r["Workgroup_Size_X"]) *
                                             int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])))
         agg[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
-    out = ["| kernel | workgroups | calls | avg ms | min ms | max ms | total ms |",
-           "|---|---|---|---|---|---|---|"]
+    out = ["| kernel | workgroups | calls | avg ms | median ms | min ms | max ms | total ms |",
+           "|---|---|---|---|---|---|---|---|"]
     for (k, wg), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
-        out.append(f"| `{k}` | {wg} | {len(v)} | {sum(v) / len(v):.4f} | {min(v):.4f} | "
-                   f"{max(v):.4f} | {sum(v):.3f} |")
+        srt = sorted(v)
+        med = srt[len(srt) // 2] if len(srt) % 2 else 0.5 * (srt[len(srt) // 2 - 1] +
+                                                               srt[len(srt) // 2])
+        out.append(f"| `{k}` | {wg} | {len(v)} | {sum(v) / len(v):.4f} | {med:.4f} | "
+                   f"{min(v):.4f} | {max(v):.4f} | {sum(v):.3f} |")
     return "\n".join([f"Command: `{command}`", "", *out])
 
 

@@ -240,27 +240,52 @@ def _long_tile_picks(w, gc, rec, stats, seed):
     return sorted(picks), len(trig), len(long_skip)
 
 
+def _ascending(m):
+    """The same kept sets with every row in ascending block order, pages
+    looked up again (the remapping ablation's walk without the HRM-first
+    order); built by sorting on the device, not by the oracle."""
+    big = torch.iinfo(torch.int32).max
+    blocks = torch.where(m.blocks < 0, torch.full_like(m.blocks, big), m.blocks)
+    blocks = torch.sort(blocks, dim=-1).values
+    blocks = torch.where(blocks == big, torch.full_like(blocks, -1), blocks).contiguous()
+    # one page per block on these cases: the page of a block is found where
+    # the original row lists it
+    order = torch.argsort(torch.where(m.blocks < 0, torch.full_like(m.blocks, big), m.blocks),
+                          dim=-1)
+    pages = torch.gather(m.pages, -1, order)
+    pages = torch.where(blocks < 0, torch.full_like(pages, -1), pages).contiguous()
+    return bk.OrderedMask(blocks=blocks, pages=pages, counts=m.counts, hrm_counts=None,
+                          capacity=m.capacity)
+
+
 LONG_SKIP_CASES = [
-    ("remap32k", {}, 1.0, 2.0),
-    ("remap32k", {}, 1.0, 6.0),
-    ("remap32k", {}, 0.3, 2.0),
-    ("remap32k", {}, 0.3, 6.0),
-    ("remap32k", {"kv_block": 128}, 1.0, 4.0),
-    ("remap128k", {}, 0.1, 8.0),
+    ("remap32k", {}, 1.0, 2.0, "kap"),
+    ("remap32k", {}, 1.0, 6.0, "kap"),
+    ("remap32k", {}, 0.3, 2.0, "kap"),
+    ("remap32k", {}, 0.3, 6.0, "kap"),
+    ("remap32k", {}, 1.0, 2.0, "ascending"),
+    ("remap32k", {}, 1.0, 4.0, "ascending"),
+    ("remap32k", {"kv_block": 128}, 1.0, 4.0, "kap"),
+    ("remap128k", {}, 0.1, 8.0, "kap"),
 ]
 
 
 @pytest.mark.parametrize("case", LONG_SKIP_CASES,
-                         ids=[f"{n}{'-kv128' if kw else ''}-b{b}-t{t}"
-                              for n, kw, b, t in LONG_SKIP_CASES])
+                         ids=[f"{n}{'-kv128' if kw else ''}-b{b}-t{t}-{o}"
+                              for n, kw, b, t, o in LONG_SKIP_CASES])
 def test_long_tile_skip_parity(case):
-    name, kw, budget, tau = case
+    name, kw, budget, tau, order = case
     w = ci.get(name).with_(**kw) if kw else ci.get(name)
-    print(f"[case] long-tile skip {name} {kw} budget={budget} tau={tau}: inputs", flush=True)
+    print(f"[case] long-tile skip {name} {kw} budget={budget} tau={tau} {order}: inputs",
+          flush=True)
     x = ci.make(w).bf16_rounded()
     prob, q, k, v = upload(x, DEV)
-    print(f"[case] long-tile skip {name} {kw} budget={budget} tau={tau}: GPU layer", flush=True)
+    print(f"[case] long-tile skip {name} {kw} budget={budget} tau={tau} {order}: GPU layer",
+          flush=True)
     m = bk.proxy_ordered_mask(prob, q, k, budget)
+    if order == "ascending":
+        assert w.block == w.page_size
+        m = _ascending(m)
     r = bk.osk_prefill(prob, q, k, v, m, tau)
     torch.cuda.synchronize()
     gb, gc = _np(m.blocks), _np(m.counts)
@@ -296,7 +321,11 @@ def test_long_tile_skip_parity(case):
         assert stats[b, h, i, 1] == int(rec[b, h, i, :cnt].sum())
         skipped += int(rec[b, h, i, :cnt].sum())
         slots += cnt
-    report(f"long-tile skip {name}{'-kv128' if kw else ''} b={budget} tau={tau}",
+    if order == "ascending":
+        for (b, h, i) in picks:
+            row = gb[b, h, i, :gc[b, h, i]]
+            assert np.all(np.diff(row) > 0)
+    report(f"long-tile skip {name}{'-kv128' if kw else ''} b={budget} tau={tau} {order}",
            tiles=len(picks), longest=int(gc.max()), refill_after_skip_rows=n_trig,
            long_rows_with_skips=n_long_skip, sampled_skipped=skipped, sampled_slots=slots,
            osk_near_threshold=near, layer_skip_ratio=round(

@@ -75,7 +75,7 @@ def test_trace_groups_launches_by_grid(tmp_path):
     md = profsum.trace_md(str(p), "cmd")
     lines = [l for l in md.splitlines() if l.startswith("| `attn")]
     assert len(lines) == 2
-    assert "| 32 | 2 | 3.0000 | 2.0000 | 4.0000 | 6.000 |" in lines[0]
+    assert "| 32 | 2 | 3.0000 | 3.0000 | 2.0000 | 4.0000 | 6.000 |" in lines[0]
     assert "| 4 | 1 | 0.5000 |" in lines[1]
 
 
