@@ -186,9 +186,12 @@ __device__ __forceinline__ void lds_barrier() {
 // page list, dense or a mask shared by the KV group, compute on every K and V
 // page the workgroup loads, which halves the page traffic per query row); NS
 // LDS stages per operand (copies run NS blocks ahead for K and NS - 1 for V).
+// Occupancy: two workgroups per CU (64 KB of LDS each) give two wavefronts
+// per SIMD for 4-wavefront tiles; 2-wavefront tiles (64 rows) get one per
+// SIMD however many fit, so they ask for one and may use the whole file.
 template <int D, int NW, int kMode, int PPB, int HP, int NS>
-__global__ __launch_bounds__(NW * HP * 64, (PPB == 1 && HP == 1) ? 2 : 1) void attn_fwd_kernel(
-    const AttnParams p) {
+__global__ __launch_bounds__(NW * HP * 64, (PPB == 1 && HP == 1 && NW >= 4) ? 2 : 1) void
+attn_fwd_kernel(const AttnParams p) {
   constexpr bool kOrdered = kMode == kModeOrdered;
   constexpr bool kLogical = kMode == kModeLogical;
   static_assert(PPB == 1 || PPB == 2, "one or two pages per logical block");
@@ -599,7 +602,11 @@ __global__ __launch_bounds__(NW * HP * 64, (PPB == 1 && HP == 1) ? 2 : 1) void a
     const bool active = sel && wave_has_rows && key0 <= wave_last;
     f32x16_t sacc[MB];
     float bm = kNegInf;
-    if (active) {
+    // The logits do not wait for the slot's block id: on the ordered and
+    // dense walks they are formed for every slot (a block outside this
+    // wave's rows is masked to -inf, the value side stays gated); only the
+    // logical walk leaves unselected blocks out.
+    if (!kLogical || active) {
       qk(st, sacc);
       bm = mask_max(j_cur, sacc);
     }
