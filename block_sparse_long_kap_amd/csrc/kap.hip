@@ -644,13 +644,46 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     if (n > 0 && k < n) {
       uint32_t prefix = top_prefix, pmask = top_bound ? 0xFFFFFFFFu : 0u;
       int need = k;
-      for (int shift = 24; shift >= 0 && !top_bound; shift -= 8) {
+      int nbits = 0;   // low bits of the k-th key still to resolve
+      if (!top_bound) {
+        // The upper halves begin with the HRM flag and the leading exponent
+        // bits of -w, which most keys share, so a radix over fixed 8-bit
+        // digits would send nearly every key of its first round to one or two
+        // bins (same-address LDS atomics).  Instead, take the group (HRM or
+        // not) that holds the k-th key, the lowest and highest key of that
+        // group, and start the radix at the highest bit where they differ.
+        const int h = sHrm[t];
+        const uint32_t grp = k <= h ? 0u : 1u;
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+        for (int e = 0; e < kPerLane; ++e) {
+          if (64 * e >= n) break;
+          if (lane + 64 * e < n && (hk[e] >> 31) == grp) {
+            lo = min(lo, hk[e]);
+            hi = max(hi, hk[e]);
+          }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+          lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+          hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+        }
+        const uint32_t diff = lo ^ hi;
+        nbits = diff == 0u ? 0 : 32 - __clz((int)diff);
+        pmask = nbits == 32 ? 0u : ~((1u << nbits) - 1u);
+        prefix = lo & pmask;
+        need = grp == 0u ? k : k - h;
+      }
+      while (nbits > 0) {
+        const int width = nbits < 8 ? nbits : 8;
+        const int shift = nbits - width;
+        const uint32_t dmask = (1u << width) - 1u;
         for (int bin = lane; bin < 256; bin += 64) sHist[t][bin] = 0;
 #pragma unroll
         for (int e = 0; e < kPerLane; ++e) {
           if (64 * e >= n) break;
           if (lane + 64 * e < n && (hk[e] & pmask) == prefix)
-            atomicAdd(&sHist[t][(hk[e] >> shift) & 255u], 1u);
+            atomicAdd(&sHist[t][(hk[e] >> shift) & dmask], 1u);
         }
         uint32_t c[4];
 #pragma unroll
@@ -677,7 +710,8 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
         digit = __shfl(digit, src);
         need = __shfl(left, src);
         prefix |= (uint32_t)digit << shift;
-        pmask |= 0xFFu << shift;
+        pmask |= dmask << shift;
+        nbits = shift;
       }
       // compact keys with upper half <= prefix to the front, keeping order
       int written = 0;
