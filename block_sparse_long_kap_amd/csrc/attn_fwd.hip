@@ -415,6 +415,29 @@ attn_fwd_kernel(const AttnParams p) {
       }
     return n;
   };
+  // The ring entries of a slot whose pages a later part of the step copies,
+  // read ahead into registers (uniform values) so that the copies do not wait
+  // for an LDS round trip after the barrier.  Any slot index maps inside the
+  // ring (entries past the count are stale and unused).
+  struct SlotRef {
+    int page[PPB];
+    int block;
+  };
+  auto slot_ref = [&](int t) -> SlotRef {
+    SlotRef r;
+#pragma unroll
+    for (int s = 0; s < PPB; ++s) r.page[s] = sSlotP[(t >> 6) & 1][(t & 63) * PPB + s];
+    r.block = (kOrdered && PPB > 1) ? sSlotB[(t >> 6) & 1][t & 63] : t;
+    return r;
+  };
+  auto copy_ref = [&](const uint16_t* pool, const SlotRef& r, int stage, bool is_k) {
+    const int j = __builtin_amdgcn_readfirstlane(r.block);
+#pragma unroll
+    for (int s = 0; s < PPB; ++s)
+      if (s == 0 || j * KVB + s * kPage < L)
+        copy_page(pool, __builtin_amdgcn_readfirstlane(r.page[s]),
+                  is_k ? kbuf(stage, s) : vbuf_of(stage, s));
+  };
 
   f32x16_t o[DBLK];
 #pragma unroll
@@ -555,12 +578,14 @@ attn_fwd_kernel(const AttnParams p) {
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
     return pair_max(mx) * c2;
   };
-  auto vote = [&](float bmx, int vb) {
-    if (skip_on) {
-      const bool pred = !row_valid || (bmx < m_true - tau_l2);
-      const bool wave_all = __all(pred);
-      if (lane == 0) sVote[vb][wave] = wave_all ? 1 : 0;
-    }
+  // returns this wavefront's own vote (uniform): without it the tile-wide AND
+  // is false whatever the other wavefronts voted
+  auto vote = [&](float bmx, int vb) -> bool {
+    if (!skip_on) return false;
+    const bool pred = !row_valid || (bmx < m_true - tau_l2);
+    const bool wave_all = __all(pred);
+    if (lane == 0) sVote[vb][wave] = wave_all ? 1 : 0;
+    return wave_all;
   };
 
   // Block loop, one workgroup barrier per visited logical block.  Step t
@@ -598,6 +623,11 @@ attn_fwd_kernel(const AttnParams p) {
     const int j_cur = slot_block(t);
     const int key0 = j_cur * KVB;
     const bool sel = selected(t);
+    // the slots whose copies this step starts (the ring holds them already)
+    const int tk = NS == 4 ? min(t + NS, cnt - 1) : t + NS;
+    const int tv = NS == 4 ? min(t + NS - 1, cnt - 1) : t + NS - 1;
+    const SlotRef ref_k = slot_ref(tk);
+    const SlotRef ref_v = slot_ref(tv);
     // some key of the block is visible to some valid row of this wave
     const bool active = sel && wave_has_rows && key0 <= wave_last;
     f32x16_t sacc[MB];
@@ -610,14 +640,14 @@ attn_fwd_kernel(const AttnParams p) {
       qk(st, sacc);
       bm = mask_max(j_cur, sacc);
     }
-    vote(bm, vb);
+    const bool own_vote = vote(bm, vb);
     // V(t) and K(t+1) were issued NS - 1 steps ago; the copies of the NS - 2
     // steps since then stay in flight
     wait_vm_c<(NS - 2) * 2 * K_PER * PPB>();
     lds_barrier();
 
     bool skip = false;
-    if (skip_on) {
+    if (own_vote) {
       int all = 1;
 #pragma unroll
       for (int w = 0; w < NW; ++w) all &= sVote[vb][hs * NW + w];
@@ -642,10 +672,8 @@ attn_fwd_kernel(const AttnParams p) {
     // the on-demand V fetch below.
     if constexpr (NS == 4) {
       advance_chunks(t + 1);
-      const int tk = min(t + NS, cnt - 1);
-      const int tv = min(t + NS - 1, cnt - 1);
-      copy_k(tk, slot_block(tk), st);
-      copy_v(tv, slot_block(tv), st_prev);
+      copy_ref(p.k_pool, ref_k, st, true);
+      copy_ref(p.v_pool, ref_v, st_prev, false);
     } else {
       // A skipped block needs no V page.  Skips come in runs (once the row
       // maxima are found, most later blocks fall below them), so V(t+1) is
@@ -657,10 +685,10 @@ attn_fwd_kernel(const AttnParams p) {
         lds_barrier();                 // every wave has read slot t's pages
       }
       advance_chunks(t + 1);
-      if (t + NS < cnt && selected(t + NS)) copy_k(t + NS, slot_block(t + NS), st);
+      if (tk < cnt && selected(tk)) copy_ref(p.k_pool, ref_k, st, true);
       v_have = false;
-      if (t + NS - 1 < cnt && selected(t + NS - 1) && !skip) {
-        copy_v(t + NS - 1, slot_block(t + NS - 1), st_prev);
+      if (tv < cnt && selected(tv) && !skip) {
+        copy_ref(p.v_pool, ref_v, st_prev, false);
         v_have = true;
       }
     }
