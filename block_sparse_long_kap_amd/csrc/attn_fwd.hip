@@ -61,6 +61,9 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
+// Last word of a raw (untyped) buffer resource on CDNA: 32-bit data format,
+// no swizzle, no index stride.
+constexpr int kBufferWord3 = 0x00020000;
 
 // The two 32-lane halves of a wavefront exchanged in one VALU instruction
 // (v_permlane32_swap): one of the returned values is the lane's own, the
@@ -383,14 +386,18 @@ attn_fwd_kernel(const AttnParams p) {
     const int c = (f % KCH) ^ PageLayout<D>::swz(r);
     coff[e] = (uint32_t)(r * D + c * 8) * 2u;
   }
+  // One buffer resource per (page, head) slice, built in scalar registers;
+  // the lane offsets stay in the same VGPRs for the whole kernel.
+  constexpr int kSliceBytes = kPage * D * 2;
   auto copy_page = [&](const uint16_t* pool, int page, unsigned char* dst) {
-    const unsigned char* base = reinterpret_cast<const unsigned char*>(
-        pool + (int64_t)page * page_stride + (int64_t)g * head_stride);
+    const uint16_t* base = pool + (int64_t)page * page_stride + (int64_t)g * head_stride;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base), (short)0, kSliceBytes, kBufferWord3);
 #pragma unroll
     for (int e = 0; e < K_PER; ++e) {
-      __builtin_amdgcn_global_load_lds(
-          static_cast<const void*>(base + coff[e]),
-          (__attribute__((address_space(3))) void*)(dst + (e * NT + wave * 64) * 16), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(dst + (e * NT + wave * 64) * 16), 16,
+          (int)coff[e], 0, 0, 0);
     }
   };
   // the pages of slot t's logical block j that hold keys of the sequence;
@@ -613,6 +620,36 @@ attn_fwd_kernel(const AttnParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  // The ring entries a step needs (its block, and the pages of the copies it
+  // starts) are read during the step before, after its barrier, and moved
+  // to scalar registers at its end, so that a step's first LDS reads are its
+  // K operands and no LDS load is pending across the loop's back edge.  The
+  // ring holds those slots by then and no refill writes their half (a refill
+  // targets the chunk 64 slots ahead).
+  struct NextRefs {
+    int block;      // slot t's logical block (ordered walk)
+    SlotRef k, v;   // the slots whose K and V pages step t copies
+  };
+  auto read_next = [&](int t) -> NextRefs {
+    NextRefs r;
+    r.block = kOrdered ? sSlotB[(t >> 6) & 1][t & 63] : t;
+    r.k = slot_ref(NS == 4 ? min(t + NS, cnt - 1) : t + NS);
+    r.v = slot_ref(NS == 4 ? min(t + NS - 1, cnt - 1) : t + NS - 1);
+    return r;
+  };
+  auto uniform_refs = [&](const NextRefs& r) -> NextRefs {
+    NextRefs u;
+    u.block = __builtin_amdgcn_readfirstlane(r.block);
+#pragma unroll
+    for (int s = 0; s < PPB; ++s) {
+      u.k.page[s] = __builtin_amdgcn_readfirstlane(r.k.page[s]);
+      u.v.page[s] = __builtin_amdgcn_readfirstlane(r.v.page[s]);
+    }
+    u.k.block = __builtin_amdgcn_readfirstlane(r.k.block);
+    u.v.block = __builtin_amdgcn_readfirstlane(r.v.block);
+    return u;
+  };
+  NextRefs nx = uniform_refs(read_next(0));
   // One step per slot; the slot's LDS stage (t % NS) is a compile-time
   // constant, so every LDS operand address is a fixed per-lane offset plus an
   // immediate.
@@ -620,14 +657,14 @@ attn_fwd_kernel(const AttnParams p) {
     constexpr int st = decltype(stage_c)::value;     // t % NS
     constexpr int vb = st & 1;                       // vote buffer, t & 1
     constexpr int st_prev = (st + NS - 1) % NS;      // stage of slot t - 1 and t + NS - 1
-    const int j_cur = slot_block(t);
+    const int j_cur = kOrdered ? nx.block : t;
     const int key0 = j_cur * KVB;
     const bool sel = selected(t);
-    // the slots whose copies this step starts (the ring holds them already)
+    // the slots whose copies this step starts
     const int tk = NS == 4 ? min(t + NS, cnt - 1) : t + NS;
     const int tv = NS == 4 ? min(t + NS - 1, cnt - 1) : t + NS - 1;
-    const SlotRef ref_k = slot_ref(tk);
-    const SlotRef ref_v = slot_ref(tv);
+    const SlotRef ref_k = nx.k;
+    const SlotRef ref_v = nx.v;
     // some key of the block is visible to some valid row of this wave
     const bool active = sel && wave_has_rows && key0 <= wave_last;
     f32x16_t sacc[MB];
@@ -697,6 +734,7 @@ attn_fwd_kernel(const AttnParams p) {
       zero_v_tail(st, L - key0);
       __syncthreads();
     }
+    const NextRefs nx_raw = read_next(t + 1);
     if (active && !skip) {
       // ---- online softmax (log2 domain) with lazy rescaling
       const float mn = fmaxf(m_true, bm);
@@ -715,6 +753,7 @@ attn_fwd_kernel(const AttnParams p) {
       lsum += softmax_p(sacc, mu, pb);
       pv(st, pb);
     }
+    nx = uniform_refs(nx_raw);
   };
   // Whole groups of NS steps in the loop, the rest after it: every path
   // around the loop issues the same copies.
