@@ -128,14 +128,15 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, int bid, int hq
   } else if (p.order == kOrderGroupXcd) {
     // group-major sequence of (group, level) units, each unit's head units on
     // one XCD (workgroup ids go round-robin over the 8 XCDs): unit u runs on
-    // XCD u % 8, each XCD takes its units in sequence order, so the heads
-    // that share the group's pages share that XCD's L2
+    // XCD u % 8, each XCD takes its units in sequence order, so the heads of
+    // a tile, whose kept pages overlap, share that XCD's L2
     const int x = bid & 7;
     const int r = bid >> 3;
     const int unit = (r / hg) * 8 + x;
     const int hh = r - (r / hg) * hg;
-    const int G = unit / p.nqb;
-    const int level = unit - G * p.nqb;
+    const int gl = unit / p.nqb;   // group within the launched range
+    const int G = p.group_begin + gl;
+    const int level = unit - gl * p.nqb;
     b = G / p.hkv;
     const int g = G - b * p.hkv;
     h = g * hg + hh;
@@ -842,7 +843,8 @@ hipError_t launch_dense_pairs(const AttnParams& p, hipStream_t stream) {
 hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, AttnMode mode,
                             hipStream_t stream) {
   // a range of groups is only defined in the group-major order
-  if (p.group_count > 0 && p.order != kOrderGroupMajor) return hipErrorInvalidValue;
+  if (p.group_count > 0 && p.order != kOrderGroupMajor && p.order != kOrderGroupXcd)
+    return hipErrorInvalidValue;
   if (COSA_HEAD_PAIRS && mode == kModeDense && p.ppb == 1 && head_dim == 128 &&
       q_block == 128 && (p.hq / p.hkv) % 2 == 0)
     return launch_dense_pairs(p, stream);

@@ -116,7 +116,7 @@ void fill_attn(cosa::AttnParams& a, const cosa_problem* p, const void* q, const 
     a.xcd_units = units % 8 == 0 ? (int32_t)units : 0;
   }
 #ifndef COSA_TILE_ORDER
-#define COSA_TILE_ORDER cosa::kOrderGroupMajor
+#define COSA_TILE_ORDER cosa::kOrderGroupXcd
 #endif
   a.order = COSA_TILE_ORDER;
   a.group_begin = 0;
@@ -422,7 +422,7 @@ COSA_EXPORT cosa_status cosa_sparse_prefill(
   a.skip_record = skip_record;
   a.row_stats = row_stats;
   a.capacity = capacity;
-  a.order = cosa::kOrderGroupMajor;   // group ranges are defined in this order
+  a.order = cosa::kOrderGroupMajor;   // group ranges need a group-major order
   if (skip_tau >= 0.f) {
     a.skip_mode = cosa::kSkipTau;
     a.tau_log2 = skip_tau * 1.4426950408889634f;
@@ -445,6 +445,8 @@ COSA_EXPORT cosa_status cosa_sparse_prefill(
     const int cnt = n_groups - g0 < chunk ? n_groups - g0 : chunk;
     k.group_begin = a.group_begin = g0;
     k.group_count = a.group_count = cnt;
+    // the heads of a tile on one XCD when the chunk's tiles split evenly
+    a.order = (int64_t)cnt * a.nqb % 8 == 0 ? cosa::kOrderGroupXcd : cosa::kOrderGroupMajor;
     e = cosa::launch_kap(k, p->head_dim, p->q_block, s0, cosa::kKapSelect);
     if (e != hipSuccess) break;
     hipStream_t s_attn = s0;

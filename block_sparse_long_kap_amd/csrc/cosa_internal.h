@@ -17,6 +17,7 @@ enum TileOrder : int32_t {
   kOrderXcdGroup = 1,   // every KV group pinned to one XCD (needs B*Hkv % 8 == 0)
   kOrderGroupMajor = 2, // one KV group after the other: its K/V stay cache-resident
   kOrderGroupXcd = 3    // group-major, the query heads of one (group, tile) on one XCD
+                        // (needs the launched groups' tile count % 8 == 0)
                         // (needs B*Hkv*NQB % 8 == 0)
 };
 
@@ -45,7 +46,7 @@ struct AttnParams {
   int32_t xcd_units;              // B*Hkv*NQB when it is a multiple of 8, else 0
   int32_t order;                  // tile order, one of TileOrder
   // (sequence, KV head) groups [group_begin, group_begin + group_count) only
-  // (group_count 0: every group); needs the group-major order
+  // (group_count 0: every group); needs a group-major order
   int32_t group_begin, group_count;
   float scale_log2;               // softmax_scale * log2(e)
   int32_t skip_mode;              // OSK: kSkipOff, kSkipTau or kSkipDelta
