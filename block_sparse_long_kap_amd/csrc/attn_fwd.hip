@@ -73,11 +73,6 @@ __device__ __forceinline__ float pair_max(float x) {
                                                   false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // K and V pages in LDS: [64 keys][D] bf16 as in HBM, with the 16-byte
 // chunks of each row permuted by a function of the row.  Pages are copied

@@ -10,6 +10,15 @@ constexpr int kPage = 64;          // tokens per KV page == logical key block
 constexpr int kProxyRows = 16;     // query rows pooled into one proxy row
 constexpr int kMaxCandidates = 2048;  // KAP: key blocks per tile handled in one pass
 
+// x plus the value of lane ^ 32, in one VALU exchange of the two 32-lane
+// halves (v_permlane32_swap returns the lane's own value and its partner's;
+// the sum is the same in either order).
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Workgroup -> (sequence, head, tile) orders of the attention kernel.  All
 // of them launch tiles with more causal blocks first.
 enum TileOrder : int32_t {

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   __shared__ float sRowInvZ[32];
   __shared__ int sHrm[TPW];          // HRM keys per tile
   __shared__ int sTopK[TPW];         // Top-p: kept count per tile
-  __shared__ uint32_t sHist[NWAVE][256];
+  __shared__ __attribute__((aligned(16))) uint32_t sHist[NWAVE][256];
   __shared__ unsigned long long sMass[kTopP ? NWAVE : 1][256];   // Top-p only
   uint16_t* sQhi = reinterpret_cast<uint16_t*>(sKeyRaw);
   uint16_t* sQlo = sQhi + 32 * D;
@@ -355,7 +355,8 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   };
   // "have rowmax" flags as a bitmap per tile (in the radix histogram space,
   // which is free until the selection)
-  uint32_t* sHrmBits = &sHist[0][0];   // [TPW][kMaxCandidates / 32]
+  // ([kMaxCandidates / 32][TPW]: one group's words of every tile side by side)
+  uint32_t* sHrmBits = &sHist[0][0];
   static_assert(TPW * (kMaxCandidates / 32) <= NWAVE * 256, "bitmap fits");
   for (int x = tid; x < TPW * (kMaxCandidates / 32); x += NT) sHrmBits[x] = 0u;
 
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
       sRowInvZ[row] = s.z > 0.f ? 1.f / s.z : 0.f;
       if (s.m != kNegInf && row < MR) {
         const int t = row / RPT;
-        atomicOr(&sHrmBits[t * (kMaxCandidates / 32) + (s.a >> 5)], 1u << (s.a & 31));
+        atomicOr(&sHrmBits[(s.a >> 5) * TPW + t], 1u << (s.a & 31));
       }
     }
   }
@@ -458,16 +459,28 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     rm[r] = sRowM[m];
     riz[r] = sRowInvZ[m];
   }
-  if (tid < TPW) sHrm[tid] = 0;
+  // HRM keys per tile, counted on its bitmap (every flagged block is a
+  // candidate of the tile), before the selection's histograms reuse that space
+  static_assert(kMaxCandidates / 32 == 64, "one bitmap word per lane");
+  if (wave < TPW) {
+    int c = __popc(sHrmBits[lane * TPW + wave]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+    if (lane == 0) sHrm[wave] = c;
+  }
   __syncthreads();
 
-  auto emit = [&](int t, int j, float wsum) {
+  // w = the sum over the tile's proxy rows / their count, as a product with
+  // the reciprocal (exact for the usual power-of-two count)
+  float inv_rows[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) inv_rows[t] = rows_t[t] > 0 ? 1.f / (float)rows_t[t] : 0.f;
+  // hrm: block j is flagged for tile t
+  auto emit = [&](int t, int j, float wsum, bool hrm) {
     const int i = i0 + t;
     unsigned long long key = ~0ull;
     if (j < n_t[t]) {
-      const float w = wsum / (float)rows_t[t];
-      const bool hrm = (sHrmBits[t * (kMaxCandidates / 32) + (j >> 5)] >> (j & 31)) & 1u;
-      if (hrm) atomicAdd(&sHrm[t], 1);
+      const float w = wsum * inv_rows[t];
       const uint32_t wb = __float_as_uint(w);   // w >= 0: bit order == value order
       key = ((unsigned long long)(hrm ? 0u : 1u) << 63) |
             ((unsigned long long)(0x7FFFFFFFu - wb) << 32) | (uint32_t)j;
@@ -479,8 +492,25 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   };
 
   // software-pipelined like pass 1
-  auto weights = [&](const f32x16_t& acc, int cb) {
+  // The group's HRM bitmap words of every tile, read at the top of the
+  // group's iteration (ahead of its products), and the flags taken out of
+  // them before the first key write, so that the key writes wait for
+  // nothing (the empty asm keeps the extraction there rather than in each
+  // tile's branch).
+  struct HrmWords {
+    uint32_t w[TPW];
+  };
+  auto hrm_words = [&](int cb) -> HrmWords {
+    HrmWords h;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) h.w[t] = sHrmBits[cb * TPW + t];
+    return h;
+  };
+  auto weights = [&](const f32x16_t& acc, int cb, const HrmWords& hw) {
     const int j = cb * 32 + col;
+    uint32_t hbits = 0;   // bit t: block j is flagged for tile t
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) hbits |= ((hw.w[t] >> col) & 1u) << t;
     float part[4];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
@@ -492,22 +522,24 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
       }
       part[g4] = sum;
     }
+    asm volatile("" : : "v"(hbits));
     if (kShared) {
       // one tile: every row of the accumulator
       const float w = part[0] + part[1] + part[2] + part[3];
-      const float wt = w + __shfl_xor(w, 32);
-      if (hf == 0) emit(0, j, wt);
+      const float wt = pair_sum(w);
+      if (hf == 0) emit(0, j, wt, hbits & 1u);
     } else if (R == 8) {
       // tile g4 = rows 8g4 .. 8g4+7: four in this lane, four in lane ^ 32
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const float w = part[g4] + __shfl_xor(part[g4], 32);
-        if (hf == 0) emit(g4, j, w);
+        const float w = pair_sum(part[g4]);
+        if (hf == 0) emit(g4, j, w, (hbits >> g4) & 1u);
       }
     } else {
       // R == 4: tile 2*g4 + hf = rows 8g4 + 4hf .. +3, all in this lane
 #pragma unroll
-      for (int g4 = 0; g4 < 2; ++g4) emit(2 * g4 + hf, j, part[g4]);
+      for (int g4 = 0; g4 < 2; ++g4)
+        emit(2 * g4 + hf, j, part[g4], (hbits >> ((2 * g4 + hf) % TPW)) & 1u);
     }
   };
   acc_cur = (f32x16_t){};
@@ -518,12 +550,14 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   }
   int cb2 = wave;
   for (; cb2 + NWAVE < nb; cb2 += NWAVE) {
+    const HrmWords hw = hrm_words(cb2);
+    __builtin_amdgcn_sched_barrier(0);
     const f32x16_t acc_next = scores();
     load_ops(min(cb2 + 2 * NWAVE, nb - 1));
-    weights(acc_cur, cb2);
+    weights(acc_cur, cb2, hw);
     acc_cur = acc_next;
   }
-  if (cb2 < nb) weights(acc_cur, cb2);
+  if (cb2 < nb) weights(acc_cur, cb2, hrm_words(cb2));
   __syncthreads();
 
   // ---- 5) top-k selection per tile (wave t handles tile t): radix-select
