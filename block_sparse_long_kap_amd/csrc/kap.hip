@@ -139,6 +139,32 @@ __device__ __forceinline__ RowStat merge(RowStat x, RowStat y) {
   return o;
 }
 
+// Inclusive prefix (sum, min or max) over the 64 lanes of a wavefront in six
+// DPP steps, without LDS: row_shr 1, 2, 4, 8 inside each row of 16 lanes
+// (lanes shifted in from outside the row contribute the identity), then
+// row_bcast:15 adds row r's last lane into row r + 1 (rows 1 and 3) and
+// row_bcast:31 lane 31 into rows 2 and 3.  Lane 63 holds the whole wave's.
+enum ScanOp { kScanAdd, kScanMin, kScanMax };
+template <ScanOp OP>
+__device__ __forceinline__ uint32_t scan_apply(uint32_t a, uint32_t b) {
+  return OP == kScanAdd ? a + b : OP == kScanMin ? (a < b ? a : b) : (a > b ? a : b);
+}
+template <ScanOp OP>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
+  constexpr int id = OP == kScanMin ? -1 : 0;   // identity (as the DPP "old" value)
+  x = scan_apply<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x111, 0xf, 0xf, false));
+  x = scan_apply<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x112, 0xf, 0xf, false));
+  x = scan_apply<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x114, 0xf, 0xf, false));
+  x = scan_apply<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x118, 0xf, 0xf, false));
+  x = scan_apply<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x142, 0xa, 0xf, false));
+  x = scan_apply<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x143, 0xc, 0xf, false));
+  return x;
+}
+template <ScanOp OP>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan<OP>(x), 63);
+}
+
 // Top-p mass of a key in fixed point: the key's w rounded down to a multiple
 // of 2^-48 (w * 2^48 is exact in fp32, the conversion truncates).
 __device__ __forceinline__ unsigned long long key_mass(uint32_t key_hi) {
@@ -359,6 +385,7 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   uint32_t* sHrmBits = &sHist[0][0];
   static_assert(TPW * (kMaxCandidates / 32) <= NWAVE * 256, "bitmap fits");
   for (int x = tid; x < TPW * (kMaxCandidates / 32); x += NT) sHrmBits[x] = 0u;
+  if (tid < TPW) sHrm[tid] = 0;   // HRM keys per tile, counted as the flags are set
 
   // ---- 3) pass 1: per-row max, arg-max (lowest block) and sum, online
   RowStat st[16];
@@ -432,12 +459,21 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
         if (mi == mx) s.a = min(s.a, sPa[base + 8 * x]);
       }
     }
+    // combine the eight threads of the row: with lane ^ 1 and lane ^ 2
+    // (quad_perm), then each quad with the other quad of its eight lanes
+    // (row_half_mirror pairs lane i with 7 - i) -- the tree of an xor
+    // butterfly, in DPP moves
 #pragma unroll
-    for (int off = 1; off < 8; off <<= 1) {
+    for (int lvl = 0; lvl < 3; ++lvl) {
+      auto partner = [&](int v) -> int {
+        return lvl == 0 ? __builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, false)
+               : lvl == 1 ? __builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, false)
+                          : __builtin_amdgcn_mov_dpp(v, 0x141, 0xf, 0xf, false);
+      };
       RowStat o;
-      o.m = __shfl_xor(s.m, off);
-      o.z = __shfl_xor(s.z, off);
-      o.a = __shfl_xor(s.a, off);
+      o.m = __int_as_float(partner(__float_as_int(s.m)));
+      o.z = __int_as_float(partner(__float_as_int(s.z)));
+      o.a = partner(s.a);
       s = merge(s, o);
     }
     if ((tid & 7) == 0) {
@@ -445,7 +481,8 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
       sRowInvZ[row] = s.z > 0.f ? 1.f / s.z : 0.f;
       if (s.m != kNegInf && row < MR) {
         const int t = row / RPT;
-        atomicOr(&sHrmBits[(s.a >> 5) * TPW + t], 1u << (s.a & 31));
+        const uint32_t bit = 1u << (s.a & 31);
+        if ((atomicOr(&sHrmBits[(s.a >> 5) * TPW + t], bit) & bit) == 0u) atomicAdd(&sHrm[t], 1);
       }
     }
   }
@@ -458,15 +495,6 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     const int m = 8 * (r >> 2) + 4 * hf + (r & 3);
     rm[r] = sRowM[m];
     riz[r] = sRowInvZ[m];
-  }
-  // HRM keys per tile, counted on its bitmap (every flagged block is a
-  // candidate of the tile), before the selection's histograms reuse that space
-  static_assert(kMaxCandidates / 32 == 64, "one bitmap word per lane");
-  if (wave < TPW) {
-    int c = __popc(sHrmBits[lane * TPW + wave]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-    if (lane == 0) sHrm[wave] = c;
   }
   __syncthreads();
 
@@ -697,11 +725,8 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
             hi = max(hi, hk[e]);
           }
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
-          hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
-        }
+        lo = wave_reduce<kScanMin>(lo);
+        hi = wave_reduce<kScanMax>(hi);
         const uint32_t diff = lo ^ hi;
         nbits = diff == 0u ? 0 : 32 - __clz((int)diff);
         pmask = nbits == 32 ? 0u : ~((1u << nbits) - 1u);
@@ -723,12 +748,7 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) c[e] = sHist[t][4 * lane + e];
         const uint32_t mine = c[0] + c[1] + c[2] + c[3];
-        uint32_t incl = mine;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t o = __shfl_up(incl, off);
-          if (lane >= off) incl += o;
-        }
+        const uint32_t incl = wave_scan<kScanAdd>(mine);
         uint32_t before = incl - mine;
         int digit = -1, left = 0;
 #pragma unroll
@@ -740,22 +760,24 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
           before += c[e];
         }
         const unsigned long long found = __ballot(digit >= 0);
-        const int src = __ffsll((long long)found) - 1;
-        digit = __shfl(digit, src);
-        need = __shfl(left, src);
+        const int src = __ffsll((long long)found) - 1;   // uniform
+        digit = __builtin_amdgcn_readlane(digit, src);
+        need = __builtin_amdgcn_readlane(left, src);
         prefix |= (uint32_t)digit << shift;
         pmask |= dmask << shift;
         nbits = shift;
       }
-      // compact keys with upper half <= prefix to the front, keeping order
+      // compact keys with upper half <= prefix to the front, keeping order;
+      // from the register copy (key idx is its upper half and idx itself)
       int written = 0;
-      for (int base = 0; base < n; base += 64) {
-        const int idx = base + lane;
-        const unsigned long long key = idx < n ? sKey[t][idx] : ~0ull;
-        const bool keep = idx < n && (uint32_t)(key >> 32) <= prefix;
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e) {
+        if (64 * e >= n) break;
+        const int idx = lane + 64 * e;
+        const bool keep = idx < n && hk[e] <= prefix;
         const unsigned long long bal = __ballot(keep);
         const int pos = written + __popcll(bal & ((1ull << lane) - 1ull));
-        if (keep) sKey[t][pos] = key;
+        if (keep) sKey[t][pos] = ((unsigned long long)hk[e] << 32) | (uint32_t)idx;
         written += __popcll(bal);
       }
       sel = written;
