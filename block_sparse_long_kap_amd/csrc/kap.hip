@@ -165,6 +165,81 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan<OP>(x), 63);
 }
 
+// The value of lane ^ S (S = 1 .. 32) in VALU cross-lane moves: quad_perm for
+// 1 and 2; within a row of 16, row_ror:12 brings lane i + 4 and row_ror:4
+// lane i - 4 (so lane ^ 4 is a choice on lane bit 2) and row_ror:8 lane i ^ 8;
+// v_permlane16_swap and v_permlane32_swap return the values of the lanes with
+// that bit clear and set, of which the partner's is the other one.
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
+  if constexpr (S == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xf, 0xf, false);
+  if constexpr (S == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xf, 0xf, false);
+  if constexpr (S == 4) {
+    const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x12C, 0xf, 0xf, false);
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xf, 0xf, false);
+    return (lane & 4) ? dn : up;
+  }
+  if constexpr (S == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, false);
+  if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  }
+  if constexpr (S == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+  return x;
+}
+
+// One compare-exchange stage of a bitonic network over 256 keys held as four
+// per lane (key e * 64 + lane in v[e]): blocks of SIZE, partner at STRIDE;
+// the lower key of a pair keeps the smaller one in ascending blocks.
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_stage(unsigned long long (&v)[4], int lane) {
+  if constexpr (STRIDE >= 64) {
+    constexpr int se = STRIDE / 64;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (e & se) continue;
+      const bool asc = ((e * 64) & SIZE) == 0;
+      const unsigned long long a = v[e], b = v[e | se];
+      const bool sw = (a > b) == asc;
+      v[e] = sw ? b : a;
+      v[e | se] = sw ? a : b;
+    }
+  } else {
+    const bool lower = (lane & STRIDE) == 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool asc = ((e * 64 + lane) & SIZE) == 0;
+      const uint32_t plo = lane_xor<STRIDE>((uint32_t)v[e], lane);
+      const uint32_t phi = lane_xor<STRIDE>((uint32_t)(v[e] >> 32), lane);
+      const unsigned long long pv = ((unsigned long long)phi << 32) | plo;
+      const bool keep_min = lower == asc;
+      const bool take = keep_min ? pv < v[e] : pv > v[e];
+      v[e] = take ? pv : v[e];
+    }
+  }
+}
+
+// Ascending sort of the first NPOW (power of two, 64 .. 256) of four keys per
+// lane: the bitonic network's stages for block sizes up to NPOW.
+template <int SIZE>
+__device__ __forceinline__ void bitonic_sizes(unsigned long long (&v)[4], int lane, int npow) {
+  if constexpr (SIZE <= 256) {
+    if (SIZE > npow) return;
+    if constexpr (SIZE >= 256) bitonic_stage<SIZE, 128>(v, lane);
+    if constexpr (SIZE >= 128) bitonic_stage<SIZE, 64>(v, lane);
+    if constexpr (SIZE >= 64) bitonic_stage<SIZE, 32>(v, lane);
+    if constexpr (SIZE >= 32) bitonic_stage<SIZE, 16>(v, lane);
+    if constexpr (SIZE >= 16) bitonic_stage<SIZE, 8>(v, lane);
+    if constexpr (SIZE >= 8) bitonic_stage<SIZE, 4>(v, lane);
+    if constexpr (SIZE >= 4) bitonic_stage<SIZE, 2>(v, lane);
+    bitonic_stage<SIZE, 1>(v, lane);
+    bitonic_sizes<SIZE * 2>(v, lane, npow);
+  }
+}
+
 // Top-p mass of a key in fixed point: the key's w rounded down to a multiple
 // of 2^-48 (w * 2^48 is exact in fp32, the conversion truncates).
 __device__ __forceinline__ unsigned long long key_mass(uint32_t key_hi) {
@@ -784,10 +859,27 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     }
 
     // ---- 6) bitonic sort of the kept keys, ascending, by this wavefront
-    // alone (LDS operations of one wavefront complete in order, so a step
-    // sees the writes of the step before it without a workgroup barrier)
+    // alone: up to 256 keys in registers (four per lane, the cross-lane
+    // partners by DPP and lane swaps), more in LDS (LDS operations of one
+    // wavefront complete in order, so a step sees the writes of the step
+    // before it without a workgroup barrier)
     int npow = 1;
     while (npow < sel) npow <<= 1;
+    if (npow <= 256) {
+      unsigned long long v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = e * 64 + lane;
+        v[e] = idx < sel ? sKey[t][idx] : ~0ull;
+      }
+      bitonic_sizes<2>(v, lane, npow);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = e * 64 + lane;
+        if (idx < npow) sKey[t][idx] = v[e];
+      }
+      npow = 0;   // nothing left for the LDS network
+    }
     for (int j = sel + lane; j < npow; j += 64) sKey[t][j] = ~0ull;
     const int half = npow >> 1;
     for (int size = 2; size <= npow; size <<= 1) {
