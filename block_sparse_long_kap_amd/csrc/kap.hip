@@ -280,8 +280,12 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   __shared__ int sTopK[TPW];         // Top-p: kept count per tile
   __shared__ __attribute__((aligned(16))) uint32_t sHist[NWAVE][256];
   __shared__ unsigned long long sMass[kTopP ? NWAVE : 1][256];   // Top-p only
+  // pooled queries, rows padded by 16 bytes so that the 32 rows' operand
+  // reads of one k-step fall on different banks
+  constexpr int kQRow = D + 8;
+  static_assert(2 * 32 * kQRow * 2 <= (int)sizeof(sKeyRaw), "pooled queries fit");
   uint16_t* sQhi = reinterpret_cast<uint16_t*>(sKeyRaw);
-  uint16_t* sQlo = sQhi + 32 * D;
+  uint16_t* sQlo = sQhi + 32 * kQRow;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -396,13 +400,17 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
           acc[2 * w + 1] += bf16_hi(v[e][t][w]);
         }
       const float f = nrow[e] > 0 ? qscale / (float)nrow[e] : 0.f;
+      u32x4_t hv, lv;   // the 8 values of the chunk, one 16-byte store per plane
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        uint16_t hi, lo;
-        split_bf16(acc[x] * f, hi, lo);
-        sQhi[m * D + c * 8 + x] = hi;
-        sQlo[m * D + c * 8 + x] = lo;
+      for (int x = 0; x < 8; x += 2) {
+        uint16_t h0, l0, h1, l1;
+        split_bf16(acc[x] * f, h0, l0);
+        split_bf16(acc[x + 1] * f, h1, l1);
+        hv[x / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lv[x / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
       }
+      *reinterpret_cast<u32x4_t*>(&sQhi[m * kQRow + c * 8]) = hv;
+      *reinterpret_cast<u32x4_t*>(&sQlo[m * kQRow + c * 8]) = lv;
     }
   }
   __syncthreads();
@@ -411,8 +419,8 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   bf16x8_t ahi[KSTEPS], alo[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    ahi[ks] = *reinterpret_cast<const bf16x8_t*>(&sQhi[col * D + ks * 16 + hf * 8]);
-    alo[ks] = *reinterpret_cast<const bf16x8_t*>(&sQlo[col * D + ks * 16 + hf * 8]);
+    ahi[ks] = *reinterpret_cast<const bf16x8_t*>(&sQhi[col * kQRow + ks * 16 + hf * 8]);
+    alo[ks] = *reinterpret_cast<const bf16x8_t*>(&sQlo[col * kQRow + ks * 16 + hf * 8]);
   }
   // every wave holds its operand before any wave writes the partial row
   // statistics into the same LDS space (a wave without candidate blocks
