@@ -139,6 +139,9 @@ __device__ __forceinline__ RowStat merge(RowStat x, RowStat y) {
   return o;
 }
 
+// A logical key block spans one or two pages (kv_block 64 or 128).
+constexpr int kMaxPagesPerBlock = 2;
+
 // Inclusive prefix (sum, min or max) over the 64 lanes of a wavefront in six
 // DPP steps, without LDS: row_shr 1, 2, 4, 8 inside each row of 16 lanes
 // (lanes shifted in from outside the row contribute the identity), then
@@ -914,7 +917,34 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
       if (n_t[t] > 0 && k_t[t] > 1) k_t[t] = sTopK[t];
   }
 
-  // ---- 7) first k entries of every tile, remapped pages, counts
+  // ---- 7) first k entries of every tile, remapped pages, counts.  The page
+  // ids of one chunk of entries of every tile are loaded before any of the
+  // chunk's stores: loads and stores share one counter, so a load issued after
+  // a store would wait for that store.
+  for (int s0 = 0; s0 < p.capacity; s0 += NT) {
+    const int s = s0 + tid;
+    int blk[TPW], pg[TPW][kMaxPagesPerBlock];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      blk[t] = -1;
+      if (s < p.capacity && s < k_t[t]) blk[t] = (int)(sKey[t][s] & 0xFFFFFFFFu);
+      // the block's pages; -1 for a page past the sequence's end
+#pragma unroll
+      for (int e = 0; e < kMaxPagesPerBlock; ++e) {
+        pg[t][e] = -1;
+        if (e < p.ppb && blk[t] >= 0 && blk[t] * kvb + e * kPage < L) pg[t][e] = pt[blk[t] * p.ppb + e];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      if (i0 + t >= p.nqb || s >= p.capacity) continue;
+      const int64_t row = mrow0 + i0 + t;
+      p.ordered_blocks[row * p.capacity + s] = blk[t];
+#pragma unroll
+      for (int e = 0; e < kMaxPagesPerBlock; ++e)
+        if (e < p.ppb) p.ordered_pages[(row * p.capacity + s) * p.ppb + e] = pg[t][e];
+    }
+  }
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int i = i0 + t;
@@ -922,17 +952,6 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
     const int64_t row = mrow0 + i;
     const int n = n_t[t];
     const int k = k_t[t];
-    for (int s = tid; s < p.capacity; s += NT) {
-      int blk = -1;
-      if (s < k) blk = (int)(sKey[t][s] & 0xFFFFFFFFu);
-      p.ordered_blocks[row * p.capacity + s] = blk;
-      // the block's pages; -1 for a page past the sequence's end
-      for (int e = 0; e < p.ppb; ++e) {
-        int pg = -1;
-        if (blk >= 0 && blk * kvb + e * kPage < L) pg = pt[blk * p.ppb + e];
-        p.ordered_pages[(row * p.capacity + s) * p.ppb + e] = pg;
-      }
-    }
     if (tid == 0) {
       p.counts[row] = k;
       if (p.hrm_counts != nullptr) p.hrm_counts[row] = min(k, sHrm[t]);
