@@ -268,14 +268,18 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   static_assert(MR <= 32, "one 32-row MFMA operand");
 
   // 16 KB of sort keys per tile.  Before the keys are built the same space
-  // holds the pooled queries (2 x 32 x D bf16), then the per-lane partial row
-  // statistics of pass 1 (max, sum, arg-max: 32 rows x kPartStride each; the
-  // stride spreads a row's partials over the LDS banks).
-  constexpr int kPartStride = 32 * NWAVE + 8;
+  // holds the pooled queries (2 x 32 rows of D bf16, each row padded by 16
+  // bytes so that the 32 rows' operand reads of one k-step fall on different
+  // banks), then the partial row statistics of pass 1 (max, sum, arg-max:
+  // 32 rows x kParts each).
+  constexpr int kParts = 2 * NWAVE;           // partials per row: lane halves x waves
+  constexpr int kQRow = D + 8;
   constexpr int kKeyWords = TPW * kMaxCandidates;
-  constexpr int kPartWords = (3 * 32 * kPartStride + 1) / 2;
-  __shared__ __attribute__((aligned(16)))
-  unsigned long long sKeyRaw[kKeyWords > kPartWords ? kKeyWords : kPartWords];
+  constexpr int kPartWords = (3 * 32 * kParts + 1) / 2;
+  constexpr int kQWords = 2 * 32 * kQRow * 2 / 8;
+  constexpr int kRawWords = kKeyWords > kPartWords ? (kKeyWords > kQWords ? kKeyWords : kQWords)
+                                                   : (kPartWords > kQWords ? kPartWords : kQWords);
+  __shared__ __attribute__((aligned(16))) unsigned long long sKeyRaw[kRawWords];
   auto sKey = reinterpret_cast<unsigned long long (*)[kMaxCandidates]>(sKeyRaw);
   __shared__ float sRowM[32];
   __shared__ float sRowInvZ[32];
@@ -283,9 +287,6 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   __shared__ int sTopK[TPW];         // Top-p: kept count per tile
   __shared__ __attribute__((aligned(16))) uint32_t sHist[NWAVE][256];
   __shared__ unsigned long long sMass[kTopP ? NWAVE : 1][256];   // Top-p only
-  // pooled queries, rows padded by 16 bytes so that the 32 rows' operand
-  // reads of one k-step fall on different banks
-  constexpr int kQRow = D + 8;
   static_assert(2 * 32 * kQRow * 2 <= (int)sizeof(sKeyRaw), "pooled queries fit");
   uint16_t* sQhi = reinterpret_cast<uint16_t*>(sKeyRaw);
   uint16_t* sQlo = sQhi + 32 * kQRow;
@@ -429,10 +430,6 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   // statistics into the same LDS space (a wave without candidate blocks
   // writes them right away)
   __syncthreads();
-  // rows held by this lane's accumulator registers: m = 8(r/4) + 4hf + r%4
-  int cand[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) cand[r] = row_cand(8 * (r >> 2) + 4 * hf + (r & 3));
 
   const int64_t slab = kbar_slab(p.n_max, D);
   const int64_t plane = (int64_t)p.batch * p.hkv * slab;
@@ -440,9 +437,9 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   const uint16_t* kb_lo = kb_hi + plane;
   const int nb = (n_wg + 31) / 32;
 
-  // pooled-key operands of candidate block cb (B of the score product); a
-  // wave loads a block while the products of the block before it run and
-  // the statistics of the one before that are updated
+  // pooled-key operands of candidate block group cb; a wave loads a group
+  // while the products of the group before it run and the statistics of the
+  // one before that are updated
   bf16x8_t kh[KSTEPS], kl[KSTEPS];
   // (blocks past the sequence's last one hold stale values; their scores
   // are masked)
@@ -454,17 +451,41 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
       kl[ks] = *reinterpret_cast<const bf16x8_t*>(kb_lo + at + ks * (2 * 32 * 8));
     }
   };
-  // scores of the loaded block for the 32 rows (log2 units)
-  auto scores = [&]() -> f32x16_t {
+  // Scores of the loaded group for the 32 proxy rows (log2 units). With the
+  // blocks as the rows of the result (block_rows), lane (col, hf) holds
+  // proxy row col for the blocks 8(r/4) + 4hf + r%4 of the group; otherwise
+  // block col for the proxy rows 8(r/4) + 4hf + r%4. With load_next, each
+  // k-step's operands are replaced by those of group `next` as soon as its
+  // three products have read them (the loads then have the rest of the
+  // chain as lead time; the interleave is pinned, since the scheduler would
+  // otherwise move every load behind the last product).
+  auto scores = [&](auto block_rows, auto load_next, int next) -> f32x16_t {
+    constexpr bool kBlockRows = decltype(block_rows)::value;
+    constexpr bool kLoadNext = decltype(load_next)::value;
     f32x16_t acc = {};
+    const int64_t at = kbar_offset<D>(next * 32 + col, hf * 8);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], kh[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], kl[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], kh[ks], acc, 0, 0, 0);
+      if constexpr (kBlockRows) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[ks], ahi[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[ks], ahi[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[ks], alo[ks], acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], kh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], kl[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], kh[ks], acc, 0, 0, 0);
+      }
+      if constexpr (kLoadNext) {
+        kh[ks] = *reinterpret_cast<const bf16x8_t*>(kb_hi + at + ks * (2 * 32 * 8));
+        kl[ks] = *reinterpret_cast<const bf16x8_t*>(kb_lo + at + ks * (2 * 32 * 8));
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // three MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // then two vector loads
+      }
     }
     return acc;
   };
+  constexpr std::true_type kRowsAreBlocks{}, kLoadNextGroup{};
+  constexpr std::false_type kRowsAreProxyRows{}, kNoLoad{};
   // "have rowmax" flags as a bitmap per tile (in the radix histogram space,
   // which is free until the selection)
   // ([kMaxCandidates / 32][TPW]: one group's words of every tile side by side)
@@ -473,78 +494,88 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   for (int x = tid; x < TPW * (kMaxCandidates / 32); x += NT) sHrmBits[x] = 0u;
   if (tid < TPW) sHrm[tid] = 0;   // HRM keys per tile, counted as the flags are set
 
-  // ---- 3) pass 1: per-row max, arg-max (lowest block) and sum, online
-  RowStat st[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) st[r] = RowStat{kNegInf, 0.f, 0x7FFFFFFF};
-  // software-pipelined: the products of block cb + NWAVE are issued before
-  // the statistics of block cb, whose vector work then overlaps them, and
-  // the operands of block cb + 2 NWAVE are loaded meanwhile (near the end
-  // the index is clamped to the last block; that load goes unused)
+  // ---- 3) pass 1: per-row max, arg-max (lowest block) and sum, online.
+  // The products put the blocks on the rows, so lane (col, hf) keeps the
+  // statistics of proxy row col over its half of every group: blocks
+  // 8(r/4) + 4hf + r%4 for r = 0..15, in ascending order.
+  const int cand_raw = row_cand(col);
+  const bool row_ok = cand_raw > 0;
+  // a row without candidates runs the unmasked path on whatever it reads;
+  // its statistics are dropped before the merge
+  const int cand_l = row_ok ? cand_raw : 0x3FFFFFFF;
+  RowStat st{kNegInf, 0.f, 0x7FFFFFFF};
+  // software-pipelined: the products of group cb + NWAVE are issued before
+  // the statistics of group cb, whose vector work then overlaps them, and
+  // the operands of group cb + 2 NWAVE are loaded meanwhile (near the end
+  // the index is clamped to the last group; that load goes unused)
   auto stats1 = [&](const f32x16_t& acc, int cb) {
-    const int j = cb * 32 + col;
+    // element r is block cb * 32 + 4hf + off(r), off(r) = 8(r/4) + r%4 <= 27
+    const int lim = cand_l - cb * 32 - 4 * hf;
+    float sv[16];
+    if (__all(lim >= 28)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // one exponential per element: exp2(-|s - m|) rescales the sum when s
-      // raises the max (blocks arrive in ascending order per lane, so a
-      // strict raise keeps the lowest block index) and is s's term otherwise
-      const float s = acc[r];
-      const float d = s - st[r].m;            // +inf while the row is empty
-      const bool up = d > 0.f;
-      const float e = __builtin_amdgcn_exp2f(up ? -d : d);
-      const float zn = up ? fmaf(st[r].z, e, 1.f) : st[r].z + e;
-      const bool valid = j < cand[r];
-      st[r].z = valid ? zn : st[r].z;
-      st[r].a = valid && up ? j : st[r].a;
-      st[r].m = valid && up ? s : st[r].m;
+      for (int r = 0; r < 16; ++r) sv[r] = acc[r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[r] = 8 * (r >> 2) + (r & 3) < lim ? acc[r] : kNegInf;
     }
+    float mx = fmaxf(sv[0], sv[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sv[r]), sv[r + 1]);
+    const float mn = fmaxf(st.m, mx);
+    const float mu = mn == kNegInf ? 0.f : mn;   // no valid score yet: every term is 0
+    float e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(sv[r] - mu);
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int r = 0; r < w; ++r) e[r] += e[r + w];
+    const float zn = fmaf(st.z, __builtin_amdgcn_exp2f(st.m - mu), e[0]);
+    if (__any(mx > st.m)) {
+      // a strict raise takes the group's lowest block reaching the new max
+      // (an equal max keeps the earlier, lower block)
+      int ai = 0x7FFFFFFF;
+#pragma unroll
+      for (int r = 15; r >= 0; --r)
+        ai = sv[r] == mx ? cb * 32 + 4 * hf + 8 * (r >> 2) + (r & 3) : ai;
+      st.a = mx > st.m ? ai : st.a;
+    }
+    st.m = mn;
+    st.z = zn;
   };
   f32x16_t acc_cur = {};
   if (wave < nb) {
     load_ops(wave);
-    acc_cur = scores();
+    acc_cur = scores(kRowsAreBlocks, kNoLoad, 0);
     if (wave + NWAVE < nb) load_ops(wave + NWAVE);
   }
   int cb1 = wave;
   for (; cb1 + NWAVE < nb; cb1 += NWAVE) {
-    const f32x16_t acc_next = scores();
-    load_ops(min(cb1 + 2 * NWAVE, nb - 1));
+    const f32x16_t acc_next = scores(kRowsAreBlocks, kLoadNextGroup, min(cb1 + 2 * NWAVE, nb - 1));
     stats1(acc_cur, cb1);
     acc_cur = acc_next;
   }
   if (cb1 < nb) stats1(acc_cur, cb1);
-  // merge the 128 partial statistics of every row (32 candidate lanes x
-  // NWAVE waves): each lane puts its 16 rows' partials into LDS, then eight
-  // threads per row merge 16 partials each (max first, then the sum rescaled
-  // to it and the lowest block index reaching it) and combine over three
-  // lane steps
+  // merge the kParts partial statistics of every row (two lane halves x
+  // NWAVE waves): eight threads per row, one partial each (max first, then
+  // the sum rescaled to it and the lowest block index reaching it), combined
+  // over three lane steps
+  static_assert(kParts == 8, "one partial per thread of a row");
   float* sPm = reinterpret_cast<float*>(sKeyRaw);
-  float* sPz = sPm + 32 * kPartStride;
-  int* sPa = reinterpret_cast<int*>(sPz + 32 * kPartStride);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int at = (8 * (r >> 2) + 4 * hf + (r & 3)) * kPartStride + wave * 32 + col;
-    sPm[at] = st[r].m;
-    sPz[at] = st[r].z;
-    sPa[at] = st[r].a;
+  float* sPz = sPm + 32 * kParts;
+  int* sPa = reinterpret_cast<int*>(sPz + 32 * kParts);
+  {
+    const int at = col * kParts + wave * 2 + hf;
+    sPm[at] = row_ok ? st.m : kNegInf;
+    sPz[at] = row_ok ? st.z : 0.f;
+    sPa[at] = row_ok ? st.a : 0x7FFFFFFF;
   }
   __syncthreads();
   {
-    constexpr int PER = 32 * NWAVE / 8;
     const int row = tid >> 3;
-    const int base = row * kPartStride + (tid & 7);
-    float mx = kNegInf;
-#pragma unroll
-    for (int x = 0; x < PER; ++x) mx = fmaxf(mx, sPm[base + 8 * x]);
-    RowStat s{mx, 0.f, 0x7FFFFFFF};
-    if (mx != kNegInf) {
-#pragma unroll
-      for (int x = 0; x < PER; ++x) {
-        const float mi = sPm[base + 8 * x];
-        if (mi != kNegInf) s.z += sPz[base + 8 * x] * __builtin_amdgcn_exp2f(mi - mx);
-        if (mi == mx) s.a = min(s.a, sPa[base + 8 * x]);
-      }
-    }
+    const int at = row * kParts + (tid & 7);
+    RowStat s{sPm[at], sPz[at], sPa[at]};
     // combine the eight threads of the row: with lane ^ 1 and lane ^ 2
     // (quad_perm), then each quad with the other quad of its eight lanes
     // (row_half_mirror pairs lane i with 7 - i) -- the tree of an xor
@@ -575,6 +606,11 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   __syncthreads();
 
   // ---- 4) pass 2: importance w and HRM flag per (tile, candidate) -> keys
+  // The products put the proxy rows on the rows: lane (col, hf) holds block
+  // col of the group for rows m = 8(r/4) + 4hf + r%4.
+  int cand[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) cand[r] = row_cand(8 * (r >> 2) + 4 * hf + (r & 3));
   float rm[16], riz[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -659,15 +695,15 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   acc_cur = (f32x16_t){};
   if (wave < nb) {
     load_ops(wave);
-    acc_cur = scores();
+    acc_cur = scores(kRowsAreProxyRows, kNoLoad, 0);
     if (wave + NWAVE < nb) load_ops(wave + NWAVE);
   }
   int cb2 = wave;
   for (; cb2 + NWAVE < nb; cb2 += NWAVE) {
     const HrmWords hw = hrm_words(cb2);
     __builtin_amdgcn_sched_barrier(0);
-    const f32x16_t acc_next = scores();
-    load_ops(min(cb2 + 2 * NWAVE, nb - 1));
+    const f32x16_t acc_next =
+        scores(kRowsAreProxyRows, kLoadNextGroup, min(cb2 + 2 * NWAVE, nb - 1));
     weights(acc_cur, cb2, hw);
     acc_cur = acc_next;
   }
