@@ -606,108 +606,162 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   __syncthreads();
 
   // ---- 4) pass 2: importance w and HRM flag per (tile, candidate) -> keys
-  // The products put the proxy rows on the rows: lane (col, hf) holds block
-  // col of the group for rows m = 8(r/4) + 4hf + r%4.
-  int cand[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) cand[r] = row_cand(8 * (r >> 2) + 4 * hf + (r & 3));
-  float rm[16], riz[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = 8 * (r >> 2) + 4 * hf + (r & 3);
-    rm[r] = sRowM[m];
-    riz[r] = sRowInvZ[m];
-  }
-  __syncthreads();
-
   // w = the sum over the tile's proxy rows / their count, as a product with
   // the reciprocal (exact for the usual power-of-two count)
   float inv_rows[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) inv_rows[t] = rows_t[t] > 0 ? 1.f / (float)rows_t[t] : 0.f;
-  // hrm: block j is flagged for tile t
-  auto emit = [&](int t, int j, float wsum, bool hrm) {
-    const int i = i0 + t;
+  // key of block j of tile t (~0 past the tile's candidates); hrm: block j
+  // is flagged for tile t
+  auto emit = [&](int t, int j, int n, float inv, float wsum, bool hrm) {
     unsigned long long key = ~0ull;
-    if (j < n_t[t]) {
-      const float w = wsum * inv_rows[t];
+    if (j < n) {
+      const float w = wsum * inv;
       const uint32_t wb = __float_as_uint(w);   // w >= 0: bit order == value order
       key = ((unsigned long long)(hrm ? 0u : 1u) << 63) |
             ((unsigned long long)(0x7FFFFFFFu - wb) << 32) | (uint32_t)j;
-      const int64_t row = mrow0 + i;
+      const int64_t row = mrow0 + i0 + t;
       if (p.debug_w != nullptr) p.debug_w[row * p.n_max + j] = w;
       if (p.debug_hrm != nullptr) p.debug_hrm[row * p.n_max + j] = hrm ? 1 : 0;
     }
     sKey[t][j] = key;   // j < nb * 32 <= kMaxCandidates
   };
-
   // software-pipelined like pass 1
-  // The group's HRM bitmap words of every tile, read at the top of the
-  // group's iteration (ahead of its products), and the flags taken out of
-  // them before the first key write, so that the key writes wait for
-  // nothing (the empty asm keeps the extraction there rather than in each
-  // tile's branch).
-  struct HrmWords {
-    uint32_t w[TPW];
-  };
-  auto hrm_words = [&](int cb) -> HrmWords {
-    HrmWords h;
+  if constexpr (!kShared) {
+    // The products put the blocks on the rows as in pass 1: lane (col, hf)
+    // holds proxy row col (tile col / R) for blocks 8(r/4) + 4hf + r%4 of
+    // the group. A tile's weight of a block is the sum over its R lanes
+    // (same hf), taken as a reduce-scatter: at each lane step the two
+    // partners keep complementary halves of the remaining blocks, so that
+    // each lane ends with 16 / R finished sums.
+    const bool lane_row = col < MR;
+    const int t_l = lane_row ? col / R : 0;
+    int n_l = 0;
+    float inv_l = 0.f;
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) h.w[t] = sHrmBits[cb * TPW + t];
-    return h;
-  };
-  auto weights = [&](const f32x16_t& acc, int cb, const HrmWords& hw) {
-    const int j = cb * 32 + col;
-    uint32_t hbits = 0;   // bit t: block j is flagged for tile t
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) hbits |= ((hw.w[t] >> col) & 1u) << t;
-    float part[4];
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      float sum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g4 + e;
-        sum += j < cand[r] ? __builtin_amdgcn_exp2f(acc[r] - rm[r]) * riz[r] : 0.f;
-      }
-      part[g4] = sum;
+    for (int t = 0; t < TPW; ++t) {
+      n_l = t_l == t ? n_t[t] : n_l;
+      inv_l = t_l == t ? inv_rows[t] : inv_l;
     }
-    asm volatile("" : : "v"(hbits));
-    if (kShared) {
-      // one tile: every row of the accumulator
-      const float w = part[0] + part[1] + part[2] + part[3];
-      const float wt = pair_sum(w);
-      if (hf == 0) emit(0, j, wt, hbits & 1u);
-    } else if (R == 8) {
-      // tile g4 = rows 8g4 .. 8g4+7: four in this lane, four in lane ^ 32
+    const float rm_l = sRowM[col];
+    const float riz_l = sRowInvZ[col];
+    const int cand_l2 = lane_row ? row_cand(col) : 0;
+    __syncthreads();
+    constexpr int EPL = 16 / R;   // finished sums per lane
+    auto weights_t = [&](const f32x16_t& acc, int cb, uint32_t hword) {
+      // element r is block cb * 32 + 4hf + off(r), off(r) = 8(r/4) + r%4 <= 27
+      const int lim = cand_l2 - cb * 32 - 4 * hf;
+      float v[16];
+      if (__all(lim >= 28)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = __builtin_amdgcn_exp2f(acc[r] - rm_l) * riz_l;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          v[r] = 8 * (r >> 2) + (r & 3) < lim ? __builtin_amdgcn_exp2f(acc[r] - rm_l) * riz_l : 0.f;
+      }
+      // lane steps: lane bit 2 against the mirror lane 7 - i (R == 8 only),
+      // then bit 1 (lane ^ 2), then bit 0 (lane ^ 1); the lane with the bit
+      // set keeps the upper half
+      int base = 0;
+      auto step = [&](auto n_c, auto ctrl_c, int bit) {
+        constexpr int N = decltype(n_c)::value;
+        constexpr int CTRL = decltype(ctrl_c)::value;
+        const bool up = (col >> bit) & 1;
+#pragma unroll
+        for (int x = 0; x < N / 2; ++x) {
+          const float send = up ? v[x] : v[x + N / 2];
+          const float keep = up ? v[x + N / 2] : v[x];
+          v[x] = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xf, 0xf, false));
+        }
+        base += up ? N / 2 : 0;
+      };
+      if constexpr (R == 8) {
+        step(std::integral_constant<int, 16>{}, std::integral_constant<int, 0x141>{}, 2);
+        step(std::integral_constant<int, 8>{}, std::integral_constant<int, 0x4E>{}, 1);
+        step(std::integral_constant<int, 4>{}, std::integral_constant<int, 0xB1>{}, 0);
+      } else {
+        static_assert(R == 4, "four or eight proxy rows per tile");
+        step(std::integral_constant<int, 16>{}, std::integral_constant<int, 0x4E>{}, 1);
+        step(std::integral_constant<int, 8>{}, std::integral_constant<int, 0xB1>{}, 0);
+      }
+      if (lane_row) {
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) {
+          const int r = base + x;
+          const int j = cb * 32 + 4 * hf + 8 * (r >> 2) + (r & 3);
+          emit(t_l, j, n_l, inv_l, v[x], (hword >> (j & 31)) & 1u);
+        }
+      }
+    };
+    acc_cur = (f32x16_t){};
+    if (wave < nb) {
+      load_ops(wave);
+      acc_cur = scores(kRowsAreBlocks, kNoLoad, 0);
+      if (wave + NWAVE < nb) load_ops(wave + NWAVE);
+    }
+    int cb2 = wave;
+    for (; cb2 + NWAVE < nb; cb2 += NWAVE) {
+      // the group's HRM bitmap word of the lane's tile, read ahead of the
+      // products
+      const uint32_t hword = sHrmBits[cb2 * TPW + t_l];
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x16_t acc_next =
+          scores(kRowsAreBlocks, kLoadNextGroup, min(cb2 + 2 * NWAVE, nb - 1));
+      weights_t(acc_cur, cb2, hword);
+      acc_cur = acc_next;
+    }
+    if (cb2 < nb) weights_t(acc_cur, cb2, sHrmBits[cb2 * TPW + t_l]);
+  } else {
+    // One tile of HPW query heads: the products put the proxy rows on the
+    // rows, lane (col, hf) holds block col of the group for rows
+    // m = 8(r/4) + 4hf + r%4, and the tile's weight is a sum inside the lane
+    // plus one lane swap.
+    int cand[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cand[r] = row_cand(8 * (r >> 2) + 4 * hf + (r & 3));
+    float rm[16], riz[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 8 * (r >> 2) + 4 * hf + (r & 3);
+      rm[r] = sRowM[m];
+      riz[r] = sRowInvZ[m];
+    }
+    __syncthreads();
+    auto weights = [&](const f32x16_t& acc, int cb, uint32_t hword) {
+      const int j = cb * 32 + col;
+      const bool hrm = (hword >> col) & 1u;
+      float part[4];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const float w = pair_sum(part[g4]);
-        if (hf == 0) emit(g4, j, w, (hbits >> g4) & 1u);
-      }
-    } else {
-      // R == 4: tile 2*g4 + hf = rows 8g4 + 4hf .. +3, all in this lane
+        float sum = 0.f;
 #pragma unroll
-      for (int g4 = 0; g4 < 2; ++g4)
-        emit(2 * g4 + hf, j, part[g4], (hbits >> ((2 * g4 + hf) % TPW)) & 1u);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          sum += j < cand[r] ? __builtin_amdgcn_exp2f(acc[r] - rm[r]) * riz[r] : 0.f;
+        }
+        part[g4] = sum;
+      }
+      const float wt = pair_sum(part[0] + part[1] + part[2] + part[3]);
+      if (hf == 0) emit(0, j, n_t[0], inv_rows[0], wt, hrm);
+    };
+    acc_cur = (f32x16_t){};
+    if (wave < nb) {
+      load_ops(wave);
+      acc_cur = scores(kRowsAreProxyRows, kNoLoad, 0);
+      if (wave + NWAVE < nb) load_ops(wave + NWAVE);
     }
-  };
-  acc_cur = (f32x16_t){};
-  if (wave < nb) {
-    load_ops(wave);
-    acc_cur = scores(kRowsAreProxyRows, kNoLoad, 0);
-    if (wave + NWAVE < nb) load_ops(wave + NWAVE);
+    int cb2 = wave;
+    for (; cb2 + NWAVE < nb; cb2 += NWAVE) {
+      const uint32_t hword = sHrmBits[cb2];
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x16_t acc_next =
+          scores(kRowsAreProxyRows, kLoadNextGroup, min(cb2 + 2 * NWAVE, nb - 1));
+      weights(acc_cur, cb2, hword);
+      acc_cur = acc_next;
+    }
+    if (cb2 < nb) weights(acc_cur, cb2, sHrmBits[cb2]);
   }
-  int cb2 = wave;
-  for (; cb2 + NWAVE < nb; cb2 += NWAVE) {
-    const HrmWords hw = hrm_words(cb2);
-    __builtin_amdgcn_sched_barrier(0);
-    const f32x16_t acc_next =
-        scores(kRowsAreProxyRows, kLoadNextGroup, min(cb2 + 2 * NWAVE, nb - 1));
-    weights(acc_cur, cb2, hw);
-    acc_cur = acc_next;
-  }
-  if (cb2 < nb) weights(acc_cur, cb2, hrm_words(cb2));
   __syncthreads();
 
   // ---- 5) top-k selection per tile (wave t handles tile t): radix-select
