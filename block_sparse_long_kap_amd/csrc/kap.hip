@@ -274,13 +274,18 @@ __global__ __launch_bounds__(256, 2) void kap_select(const KapParams p) {
   // 32 rows x kParts each).
   constexpr int kParts = 2 * NWAVE;           // partials per row: lane halves x waves
   constexpr int kQRow = D + 8;
-  constexpr int kKeyWords = TPW * kMaxCandidates;
+  // A tile's keys start one 8-byte key further along the banks than the
+  // tile before's: a pass-2 key write of a wavefront puts 16 keys of each
+  // tile at even (or odd) key positions modulo 32, the same for every tile,
+  // which the odd offset spreads over both halves of the banks.
+  constexpr int kKeyStride = kMaxCandidates + 1;
+  constexpr int kKeyWords = TPW * kKeyStride;
   constexpr int kPartWords = (3 * 32 * kParts + 1) / 2;
   constexpr int kQWords = 2 * 32 * kQRow * 2 / 8;
   constexpr int kRawWords = kKeyWords > kPartWords ? (kKeyWords > kQWords ? kKeyWords : kQWords)
                                                    : (kPartWords > kQWords ? kPartWords : kQWords);
   __shared__ __attribute__((aligned(16))) unsigned long long sKeyRaw[kRawWords];
-  auto sKey = reinterpret_cast<unsigned long long (*)[kMaxCandidates]>(sKeyRaw);
+  auto sKey = reinterpret_cast<unsigned long long (*)[kKeyStride]>(sKeyRaw);
   __shared__ float sRowM[32];
   __shared__ float sRowInvZ[32];
   __shared__ int sHrm[TPW];          // HRM keys per tile
