@@ -124,7 +124,7 @@ def main():
                       num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                       head_dim=w.head_dim, max_seqlen=w.max_seqlen, total_q=w.total_tokens,
                       num_pages=x.k_pool.shape[0], q_block=w.q_block, page_size=w.page_size,
-                      softmax_scale=w.softmax_scale)
+                      kv_block=w.block, softmax_scale=w.softmax_scale)
     ws = bk.KapWorkspace(prob)
     mask = bk.proxy_ordered_mask(prob, q, kp, budget, workspace=ws)
     rec = bk.osk_prefill(prob, q, kp, vp, mask, tau, record=True)
@@ -135,13 +135,13 @@ def main():
     visited = int(stats[:, 0].sum())
     skipped = int(stats[:, 1].sum())
     computed = visited - skipped
-    fps = flops_per_slot(w.q_block, w.head_dim, w.page_size)
+    fps = flops_per_slot(w.q_block, w.head_dim, w.block)
     osk_flops = fps * (visited + computed)
     lens = np.diff(x.cu_seqlens)
     causal_slots = 0
     for L in lens:
         for i in range((int(L) + w.q_block - 1) // w.q_block):
-            causal_slots += (min((i + 1) * w.q_block, int(L)) - 1) // w.page_size + 1
+            causal_slots += (min((i + 1) * w.q_block, int(L)) - 1) // w.block + 1
     causal_slots *= w.num_q_heads
     dense_flops = 2 * fps * causal_slots
 
@@ -410,7 +410,7 @@ def stage2_measurement(args, bk, torch, dev, stream, ev, dense_ms, headline):
                       num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                       head_dim=w.head_dim, max_seqlen=w.max_seqlen, total_q=w.total_tokens,
                       num_pages=x.k_pool.shape[0], q_block=w.q_block, page_size=w.page_size,
-                      softmax_scale=w.softmax_scale)
+                      kv_block=w.block, softmax_scale=w.softmax_scale)
     lens = np.diff(x.cu_seqlens)
     del x
     ws = bk.KapWorkspace(prob)
@@ -424,9 +424,9 @@ def stage2_measurement(args, bk, torch, dev, stream, ev, dense_ms, headline):
     causal = 0
     for L in lens:
         for i in range((int(L) + w.q_block - 1) // w.q_block):
-            causal += (min((i + 1) * w.q_block, int(L)) - 1) // w.page_size + 1
+            causal += (min((i + 1) * w.q_block, int(L)) - 1) // w.block + 1
     causal *= w.num_q_heads
-    fps = flops_per_slot(w.q_block, w.head_dim, w.page_size)
+    fps = flops_per_slot(w.q_block, w.head_dim, w.block)
 
     def timed(fn, n):
         for _ in range(max(1, args.warmup)):

@@ -157,6 +157,10 @@ REMAP_128K = LLAMA_128K.with_(
     budgets_sweep=(0.3, 0.1), taus_sweep=(2.0, 4.0, 6.0, 8.0),
 )
 
+# The llama128k layer over logical key blocks of 128 keys (two 64-token pages
+# each): half the candidate blocks for the proxy, the same budget fraction.
+LLAMA_128K_KV128 = LLAMA_128K.with_(name="llama128k_kv128", kv_block=128)
+
 # Test-only variant of the tiny case with a strong sink so that the in-kernel
 # skip actually fires (sink logit around 16 nats); not a benchmark workload.
 TINY_SKIP = TINY.with_(
@@ -167,7 +171,7 @@ TINY_SKIP = TINY.with_(
 
 WORKLOADS: Dict[str, Workload] = {
     w.name: w for w in (TINY, LLAMA_32K, LLAMA_128K, QWEN_128K, STRESS, REMAP_32K, REMAP_128K,
-                         TINY_SKIP)
+                         LLAMA_128K_KV128, TINY_SKIP)
 }
 
 
