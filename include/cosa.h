@@ -276,7 +276,9 @@ cosa_status cosa_proxy_ordered_mask_shared_kv(const cosa_problem* p, const void*
  * row_stats  device int32 [rows][2] nullable: (visited slots, skipped slots).
  * Every listed block id must lie in [0, ceil(L_b / kv_block)) for its
  * sequence and every page id of a page holding keys of the sequence in
- * [0, num_pages).  With kv_block = 2 * page_size the vote and the skip cover
+ * [0, num_pages); counts[row] must lie in [0, min(capacity, the number of
+ * logical blocks the tile's last row sees)], which is at most 16384 (the
+ * kernel keeps one skip bit per slot of a tile in LDS and does not check).  With kv_block = 2 * page_size the vote and the skip cover
  * the whole 128-key logical block (the pages' b = 128, App. D.1).
  */
 cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, const void* k_pool,

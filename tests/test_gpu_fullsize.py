@@ -390,3 +390,110 @@ def test_stress_full_budget_skip_off_equals_dense():
            kernel_mean_abs=f"{mean:.2e}")
     so.assert_ok(label="stress beta=1 osk vs oracle dense")
     sl.assert_ok(max_abs=1e-3, mean_abs=1e-4, label="stress beta=1 osk lse")
+
+
+# The longest sequence the ABI accepts (2^20 tokens: 16384 key blocks, the
+# size of the kernel's per-tile skip bitmap), beyond the proxy's 2048-block
+# range, with masks built on the host.  Band-structured input (the remap128k
+# pattern) so that the in-kernel skip fires on mixed-order walks.
+MAXLEN = ci.get("remap128k").with_(name="max1m", seqlens=(1 << 20,), num_q_heads=2,
+                                   num_kv_heads=1, seed=21)
+
+
+def _max_len_mask(w, x, seed):
+    """Ordered mask rows for every (head, tile): the diagonal block then five
+    distinct earlier blocks in a seeded order; three long rows: every causal
+    block of the last tile of head 0 shuffled (16384 slots, the slot ring
+    refilled 256 times), 4096 of the 8192 blocks of a middle tile of head 1
+    shuffled after its diagonal block, and every block of an early tile of
+    head 0 in ascending order."""
+    rng = np.random.default_rng(seed)
+    L = int(x.seqlens[0])
+    nqb = (L + w.q_block - 1) // w.q_block
+    n_of = lambda i: (min((i + 1) * w.q_block, L) - 1) // w.block + 1  # noqa: E731
+    cap = n_of(nqb - 1)
+    long_rows = {}
+    i0 = nqb - 1
+    long_rows[(0, i0)] = rng.permutation(n_of(i0))
+    i1 = nqb // 2 - 1
+    n1 = n_of(i1)
+    long_rows[(1, i1)] = np.concatenate([[n1 - 1], rng.choice(n1 - 1, size=4095, replace=False)])
+    i2 = nqb // 4 - 1
+    long_rows[(0, i2)] = np.arange(n_of(i2))
+    blocks = np.full((1, w.num_q_heads, nqb, cap), -1, dtype=np.int32)
+    counts = np.zeros((1, w.num_q_heads, nqb), dtype=np.int32)
+    for h in range(w.num_q_heads):
+        for i in range(nqb):
+            n = n_of(i)
+            if (h, i) in long_rows:
+                row = long_rows[(h, i)]
+            else:
+                k = min(n, 6)
+                row = np.concatenate([[n - 1], rng.choice(n - 1, size=k - 1, replace=False)])
+            blocks[0, h, i, :len(row)] = row
+            counts[0, h, i] = len(row)
+    pt = x.page_table[0]
+    pages = np.where(blocks >= 0, pt[np.maximum(blocks, 0)], -1).astype(np.int32)
+    return blocks, pages, counts, cap, sorted(long_rows)
+
+
+def test_osk_max_seqlen_host_mask():
+    w = MAXLEN
+    print("[case] 2^20-token sequence, host masks: inputs", flush=True)
+    x = ci.make(w).bf16_rounded()
+    prob, q, k, v = upload(x, DEV)
+    blocks, pages, counts, cap, long_rows = _max_len_mask(w, x, seed=w.seed + 1)
+    mask = bk.OrderedMask(blocks=torch.from_numpy(blocks).to(DEV),
+                          pages=torch.from_numpy(pages).to(DEV),
+                          counts=torch.from_numpy(counts).to(DEV), hrm_counts=None, capacity=cap)
+    print(f"[case] 2^20-token sequence: GPU, skip off and tau 8 (capacity {cap})", flush=True)
+    r_off = bk.osk_prefill(prob, q, k, v, mask, -1.0)
+    r_on = bk.osk_prefill(prob, q, k, v, mask, w.tau)
+    torch.cuda.synchronize()
+    res = {}
+    for name, r in (("off", r_off), ("on", r_on)):
+        res[name] = (_np(r.out), _np(r.lse), _np(r.skip_record), _np(r.row_stats))
+    del mask, r_off, r_on, q, k, v
+    for name, (out, lse, rec, stats) in res.items():
+        assert np.all(np.isfinite(out)), name
+        assert np.array_equal(stats[..., 0], counts), name
+    assert int(res["off"][3][..., 1].sum()) == 0
+    n_skip = int(res["on"][3][..., 1].sum())
+    assert n_skip > 0, "the skip never fires"
+    L = int(x.seqlens[0])
+    kk = materialise(x.k_pool, x.page_table[0], L, w.page_size)[:, 0]
+    vv = materialise(x.v_pool, x.page_table[0], L, w.page_size)[:, 0]
+    rng = np.random.default_rng(w.seed + 2)
+    nqb = blocks.shape[2]
+    short = [(int(rng.integers(2)), int(rng.integers(nqb))) for _ in range(6)]
+    print(f"[case] 2^20-token sequence: oracle on {len(long_rows) + len(short)} tiles",
+          flush=True)
+    so_off, sl_off, so_on, sl_on = ErrStats(), ErrStats(), ErrStats(), ErrStats()
+    near = 0
+    for (h, i) in long_rows + short:
+        rows = np.arange(i * w.q_block, min((i + 1) * w.q_block, L))
+        qr = x.q[rows, h].astype(np.float64)
+        cnt = int(counts[0, h, i])
+        bl = blocks[0, h, i, :cnt]
+        # skip off: attention over the keys of the listed blocks
+        key_ok = np.zeros(L, dtype=bool)
+        for j in bl:
+            key_ok[j * w.block:min((j + 1) * w.block, L)] = True
+        o, ls = odense.attention_rows(qr, rows, kk, vv, w.softmax_scale, key_ok=key_ok)
+        out, lse, rec, _ = res["off"]
+        so_off.add(out[rows, h], o)
+        sl_off.add(lse[h, rows], ls)
+        # tau 8: the closed form of the skip (the 16384-slot row only above)
+        if cnt > 8192:
+            continue
+        tr = oosk.osk_tile_closed_form(qr, rows, kk, vv, bl, w.tau, w.softmax_scale, w.block)
+        out, lse, rec, _ = res["on"]
+        near += check_osk_tile(out[rows, h], lse[h, rows], rec[0, h, i], tr, qr, rows, kk, vv,
+                               bl, w.softmax_scale, w.block, so_on, sl_on)
+    report("2^20-token sequence, host masks", tiles=len(long_rows) + len(short),
+           capacity=cap, longest=int(counts.max()), layer_skipped=n_skip,
+           osk_near_threshold=near)
+    so_off.assert_ok(label="2^20 skip off out")
+    sl_off.assert_ok(max_abs=1e-3, mean_abs=1e-4, label="2^20 skip off lse")
+    so_on.assert_ok(label="2^20 tau 8 out")
+    sl_on.assert_ok(max_abs=1e-3, mean_abs=1e-4, label="2^20 tau 8 lse")
