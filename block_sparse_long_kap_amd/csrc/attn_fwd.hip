@@ -189,7 +189,8 @@ __device__ __forceinline__ void lds_barrier() {
 // per SIMD for 4-wavefront tiles; 2-wavefront tiles (64 rows) get one per
 // SIMD however many fit, so they ask for one and may use the whole file.
 template <int D, int NW, int kMode, int PPB, int HP, int NS>
-__global__ __launch_bounds__(NW * HP * 64, (PPB == 1 && HP == 1 && NW >= 4) ? 2 : 1) void
+__global__ __launch_bounds__(NW * (PPB == 2 ? 2 : HP) * 64,
+                             (PPB == 1 && HP == 1 && NW >= 4) ? 2 : 1) void
 attn_fwd_kernel(const AttnParams p) {
   constexpr bool kOrdered = kMode == kModeOrdered;
   constexpr bool kLogical = kMode == kModeLogical;
@@ -200,7 +201,15 @@ attn_fwd_kernel(const AttnParams p) {
   static_assert(HP == 1 || !kLogical, "logical skipping walks one head per workgroup");
   constexpr int KVB = kPage * PPB;                   // keys per logical block
   constexpr int MB = 2 * PPB;                        // 32-key S^T blocks per logical block
-  constexpr int NWT = NW * HP;                       // wavefronts per workgroup
+  // Two-page blocks: the two wavefronts of a pair take the same 32 query rows
+  // and one page of the block each (twice the wavefronts per workgroup, one
+  // page of products each), vote on their own page and share their row
+  // maxima, so that both keep the same running max; their partial outputs
+  // are added at the end.
+  constexpr bool kPair = PPB == 2;
+  constexpr int NGRP = kPair ? 2 : HP;               // groups of NW wavefronts
+  constexpr int MBW = kPair ? 2 : MB;                // S^T blocks per wavefront and step
+  constexpr int NWT = NW * NGRP;                     // wavefronts per workgroup
   constexpr int NT = NWT * 64;
   constexpr int NTH = NW * 64;                       // threads per head
   constexpr int BQ = NW * 32;                        // query rows per head (the tile)
@@ -231,6 +240,8 @@ attn_fwd_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char sV2[kXtra];
   __shared__ __attribute__((aligned(16))) unsigned char sV3[kXtra];
   __shared__ int sVote[2][NWT];
+  // two-page blocks: each page half's block row maxima, per vote buffer
+  __shared__ float sBm[2][2][kPair ? NW * 32 : 1];
   __shared__ int sSlotP[2][64 * PPB];   // [ring chunk][slot * PPB + page]
   __shared__ int sSlotB[2][64];         // [ring chunk][slot]: logical block
   // logical-skip mode: the tile's block bitmask (up to 16384 causal blocks)
@@ -245,16 +256,21 @@ attn_fwd_kernel(const AttnParams p) {
     const int x = stage * PPB + s;
     return x == 0 ? sV0 : x == 1 ? sV1 : x == 2 ? sV2 : sV3;
   };
+  auto kraw = [&](int x) -> unsigned char* {
+    return x == 0 ? sK0 : x == 1 ? sK1 : x == 2 ? sK2 : sK3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // uniform by construction; telling the compiler keeps the LDS destinations
   // of the page copies and the head selection in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hs = wave / NW;                          // head of the workgroup's unit
-  const int wv = wave - hs * NW;                     // wavefront within the head's tile
-  const int tid_h = tid - hs * NTH;                  // thread within the head
-  const bool head_writer = tid_h == 0;
+  const int grp = wave / NW;                         // group of NW wavefronts
+  const int hs = kPair ? 0 : grp;                    // head of the workgroup's unit
+  const int ph = kPair ? grp : 0;                    // two-page blocks: this wavefront's page
+  const int wv = wave - grp * NW;                    // wavefront within the tile
+  const int tid_h = tid - grp * NTH;                 // thread within the group
+  const bool head_writer = tid_h == 0 && ph == 0;
   const int hf = lane >> 5;
   const int col = lane & 31;
 
@@ -462,14 +478,15 @@ attn_fwd_kernel(const AttnParams p) {
   // block mb holds keys 32mb.. of the logical block (page mb / 2).  The K
   // operand reads run two k-steps ahead of the products (one with two heads
   // per workgroup, whose wavefronts hold more state).
-  auto qk = [&](int stage, f32x16_t (&sacc)[MB]) {
+  auto qk = [&](int stage, f32x16_t (&sacc)[MBW]) {
     constexpr int kAhead = HP == 1 ? 2 : 1;
-    u32x4_t a[kAhead + 1][MB];
+    u32x4_t a[kAhead + 1][MBW];
     auto load = [&](int ks) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MBW; ++mb)
         a[ks % (kAhead + 1)][mb] = *reinterpret_cast<const u32x4_t*>(
-            kbuf(stage, mb >> 1) + PageLayout<D>::offset((mb & 1) * 32 + col, 2 * ks + hf));
+            kbuf(stage, kPair ? ph : mb >> 1) +
+            PageLayout<D>::offset((mb & 1) * 32 + col, 2 * ks + hf));
     };
 #pragma unroll
     for (int ks = 0; ks < kAhead && ks < KSTEPS; ++ks) load(ks);
@@ -477,26 +494,26 @@ attn_fwd_kernel(const AttnParams p) {
     for (int ks = 0; ks < KSTEPS; ++ks) {
       if (ks + kAhead < KSTEPS) load(ks + kAhead);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MBW; ++mb)
         sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, a[ks % (kAhead + 1)][mb]), qf[ks],
             ks == 0 ? (f32x16_t){} : sacc[mb], 0, 0, 0);
     }
     // scheduling pattern: the first kAhead + 1 k-steps of reads, then one
     // k-step of products and one of reads in turn, then the last products
-    __builtin_amdgcn_sched_group_barrier(0x100, (kAhead + 1) * MB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, (kAhead + 1) * MBW, 0);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS - kAhead - 1; ++ks) {
-      __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, MB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MBW, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, MBW, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, (kAhead + 1) * MB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, (kAhead + 1) * MBW, 0);
   };
   // P = exp2(S * scale_log2 - mu) rounded to bf16 (the P^T operand), row sum
-  auto softmax_p = [&](const f32x16_t (&sacc)[MB], float mu, bf16x8_t (&pb)[2 * MB]) -> float {
+  auto softmax_p = [&](const f32x16_t (&sacc)[MBW], float mu, bf16x8_t (&pb)[2 * MBW]) -> float {
     float part = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int mb = 0; mb < MBW; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mb][r], c2, -mu));
@@ -526,10 +543,10 @@ attn_fwd_kernel(const AttnParams p) {
       }
     }
   }
-  auto pv = [&](int stage, const bf16x8_t (&pb)[2 * MB]) {
+  auto pv = [&](int stage, const bf16x8_t (&pb)[2 * MBW]) {
 #pragma unroll
-    for (int ks = 0; ks < 4 * PPB; ++ks) {
-      const unsigned char* vb = vbuf_of(stage, ks >> 2);
+    for (int ks = 0; ks < 2 * MBW; ++ks) {
+      const unsigned char* vb = vbuf_of(stage, kPair ? ph : ks >> 2);
 #pragma unroll
       for (int md = 0; md < DBLK; ++md) {
         u32x4_t a;
@@ -562,12 +579,14 @@ attn_fwd_kernel(const AttnParams p) {
   };
   // causal / end-of-sequence mask (diagonal and tail blocks only), then the
   // row's block max in log2 units
-  auto mask_max = [&](int block, f32x16_t (&sacc)[MB]) -> float {
-    const int key0 = block * KVB;
-    if ((key0 + KVB - 1 > wave_q0) || (key0 + KVB > L)) {
+  auto mask_max = [&](int block, f32x16_t (&sacc)[MBW]) -> float {
+    // keys of this wavefront's share of the block
+    const int key0 = block * KVB + (kPair ? ph * kPage : 0);
+    constexpr int KW = kPair ? kPage : KVB;
+    if ((key0 + KW - 1 > wave_q0) || (key0 + KW > L)) {
       const int lim = min(qpos, L - 1) - key0 - 4 * hf;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int koff = mb * 32 + 8 * (r >> 2) + (r & 3);
@@ -576,7 +595,7 @@ attn_fwd_kernel(const AttnParams p) {
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
     return pair_max(mx) * c2;
@@ -663,7 +682,7 @@ attn_fwd_kernel(const AttnParams p) {
     const SlotRef ref_v = nx.v;
     // some key of the block is visible to some valid row of this wave
     const bool active = sel && wave_has_rows && key0 <= wave_last;
-    f32x16_t sacc[MB];
+    f32x16_t sacc[MBW];
     float bm = kNegInf;
     // The logits do not wait for the slot's block id: on the ordered and
     // dense walks they are formed for every slot (a block outside this
@@ -673,17 +692,26 @@ attn_fwd_kernel(const AttnParams p) {
       qk(st, sacc);
       bm = mask_max(j_cur, sacc);
     }
+    // (two-page blocks: this wavefront's page only; the block is skipped
+    // when both pages are, since its max is below the threshold exactly when
+    // both pages' maxima are)
     const bool own_vote = vote(bm, vb);
+    if constexpr (kPair) {
+      if (hf == 0) sBm[vb][ph][wv * 32 + col] = bm;
+    }
     // V(t) and K(t+1) were issued NS - 1 steps ago; the copies of the NS - 2
     // steps since then stay in flight
     wait_vm_c<(NS - 2) * 2 * K_PER * PPB>();
     lds_barrier();
+    // the block's row max over both pages
+    if constexpr (kPair) bm = fmaxf(bm, sBm[vb][1 - ph][wv * 32 + col]);
 
     bool skip = false;
     if (own_vote) {
       int all = 1;
+      constexpr int NV = kPair ? NWT : NW;   // wavefronts that vote on this block
 #pragma unroll
-      for (int w = 0; w < NW; ++w) all &= sVote[vb][hs * NW + w];
+      for (int w = 0; w < NV; ++w) all &= sVote[vb][(kPair ? 0 : hs * NW) + w];
       skip = __builtin_amdgcn_readfirstlane(all) != 0;   // uniform over the head
     }
     if (kOrdered) {
@@ -745,7 +773,7 @@ attn_fwd_kernel(const AttnParams p) {
         for (int md = 0; md < DBLK; ++md) o[md] *= alpha;
       }
       const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
-      bf16x8_t pb[2 * MB];
+      bf16x8_t pb[2 * MBW];
       lsum += softmax_p(sacc, mu, pb);
       pv(st, pb);
     }
@@ -768,9 +796,33 @@ attn_fwd_kernel(const AttnParams p) {
     if (t0 + 2 < cnt) step(t0 + 2, std::integral_constant<int, 2>{});
   }
 
+  // ---- two-page blocks: page half 1 adds its partial O and row sums into
+  // half 0's through LDS (the page buffers are free after the last step;
+  // both halves hold the same running max and reference)
+  if constexpr (kPair) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();   // every wavefront is past its last read of the pages
+    float* xo = reinterpret_cast<float*>(kraw(wv));
+    float* xl = reinterpret_cast<float*>(sV0) + wv * 64;
+    if (ph == 1) {
+#pragma unroll
+      for (int md = 0; md < DBLK; ++md)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(md * 16 + r) * 64 + lane] = o[md][r];
+      xl[lane] = lsum;
+    }
+    __syncthreads();
+    if (ph == 0) {
+#pragma unroll
+      for (int md = 0; md < DBLK; ++md)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[md][r] += xo[(md * 16 + r) * 64 + lane];
+      lsum += xl[lane];
+    }
+  }
   // ---- epilogue: out = O / l, lse = m + ln l
   const float ltot = pair_sum(lsum);
-  if (row_valid) {
+  if (row_valid && ph == 0) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     uint16_t* dst = p.out + ((int64_t)(q0 + qpos) * p.hq + h) * D;
 #pragma unroll
@@ -801,7 +853,9 @@ attn_fwd_kernel(const AttnParams p) {
   if (kOrdered && p.skip_record != nullptr) {
     __syncthreads();   // every head writer's last record word is in LDS
     uint8_t* rec = p.skip_record + row * p.capacity;
-    for (int t = tid_h; t < cnt; t += NTH) rec[t] = (uint8_t)((sRec[hs][t >> 5] >> (t & 31)) & 1u);
+    if (ph == 0)
+      for (int t = tid_h; t < cnt; t += NTH)
+        rec[t] = (uint8_t)((sRec[hs][t >> 5] >> (t & 31)) & 1u);
   }
 }
 
@@ -810,8 +864,9 @@ hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const int64_t n_groups = p.group_count > 0 ? p.group_count : (int64_t)p.batch * p.hkv;
   const int64_t grid = n_groups * (p.hq / p.hkv / HP) * p.nqb;
   if (grid <= 0) return hipSuccess;
+  // two-page blocks: a pair of wavefronts per 32 query rows
   hipLaunchKernelGGL((attn_fwd_kernel<D, NW, kMode, PPB, HP, NS>), dim3((unsigned)grid),
-                     dim3(NW * HP * 64), 0, stream, p);
+                     dim3(NW * (PPB == 2 ? 2 : HP) * 64), 0, stream, p);
   return hipGetLastError();
 }
 
