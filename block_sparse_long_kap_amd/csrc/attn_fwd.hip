@@ -180,7 +180,8 @@ __device__ __forceinline__ void lds_barrier() {
 // Template parameters: D head dim; NW wavefronts per query head, 32 query
 // rows each (the tile is 32 NW rows of one head); kMode the page walk; PPB
 // pages per logical key block (1: a 64-key block is one page; 2: a 128-key
-// block is resolved through two pages, with one vote per block); HP query
+// block is resolved through two pages, with one decision per block, and each
+// 32 rows are taken by a pair of wavefronts, one page each); HP query
 // heads per workgroup (2: two query heads of one KV group that walk the same
 // page list, dense or a mask shared by the KV group, compute on every K and V
 // page the workgroup loads, which halves the page traffic per query row); NS
@@ -188,6 +189,8 @@ __device__ __forceinline__ void lds_barrier() {
 // Occupancy: two workgroups per CU (64 KB of LDS each) give two wavefronts
 // per SIMD for 4-wavefront tiles; 2-wavefront tiles (64 rows) get one per
 // SIMD however many fit, so they ask for one and may use the whole file.
+// Two-page blocks (128 KB of LDS, one workgroup per CU) get their second
+// wavefront per SIMD from the pairs.
 template <int D, int NW, int kMode, int PPB, int HP, int NS>
 __global__ __launch_bounds__(NW * (PPB == 2 ? 2 : HP) * 64,
                              (PPB == 1 && HP == 1 && NW >= 4) ? 2 : 1) void
