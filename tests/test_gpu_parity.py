@@ -476,11 +476,15 @@ def test_osk_shared_kv_masks(tau):
 
 
 KV128 = dict(RAGGED, kv_block=128, seqlens=(1, 63, 64, 65, 127, 128, 129, 200, 383))
+# every (head_dim, q_block) instance of the two-page kernel (wavefront pairs
+# of 4 or 2 row groups)
+KV128_SHAPES = [(128, 128), (128, 64), (64, 128), (64, 64)]
 
 
-def test_dense_kv_block_128_matches_oracle():
-    w, x = _inputs("tiny", **KV128)
-    print("[case] dense kv_block=128", flush=True)
+@pytest.mark.parametrize("head_dim,q_block", KV128_SHAPES)
+def test_dense_kv_block_128_matches_oracle(head_dim, q_block):
+    w, x = _inputs("tiny", **dict(KV128, head_dim=head_dim, q_block=q_block))
+    print(f"[case] dense kv_block=128 D={head_dim} q_block={q_block}", flush=True)
     prob, q, k, v = upload(x, DEV)
     res = bk.dense_prefill(prob, q, k, v)
     torch.cuda.synchronize()
@@ -492,9 +496,11 @@ def test_dense_kv_block_128_matches_oracle():
     ls.assert_ok(max_abs=1e-3, mean_abs=1e-4, label="dense kv_block=128 lse")
 
 
-def test_osk_kv_block_128_full_budget_and_shuffled():
-    w, x = _inputs("tiny", **KV128)
-    print("[case] osk kv_block=128 full budget, shuffled", flush=True)
+@pytest.mark.parametrize("head_dim,q_block", KV128_SHAPES)
+def test_osk_kv_block_128_full_budget_and_shuffled(head_dim, q_block):
+    w, x = _inputs("tiny", **dict(KV128, head_dim=head_dim, q_block=q_block))
+    print(f"[case] osk kv_block=128 D={head_dim} q_block={q_block} full budget, shuffled",
+          flush=True)
     blocks, counts = oosk.dense_order_mask(x.cu_seqlens, w.num_q_heads, w.q_block, w.block)
     _run_osk_vs_oracle(w, x, blocks, counts, -1.0, "osk kv128 full")
     rng = np.random.default_rng(1)
