@@ -238,7 +238,8 @@ def _kap_compare(w, x, budget, label, tiles=None, debug=True):
 
 @pytest.mark.parametrize("case", [("tiny", {}, 0.5), ("tiny_skip", {}, 0.5),
                                   ("tiny", dict(RAGGED), 0.3), ("tiny", dict(RAGGED), 1.0),
-                                  ("tiny", dict(RAGGED, q_block=64), 0.05)])
+                                  ("tiny", dict(RAGGED, q_block=64), 0.05),
+                                  ("tiny", dict(RAGGED, head_dim=64), 0.3)])
 def test_kap_matches_oracle(case):
     name, kw, budget = case
     w, x = _inputs(name, **kw)
@@ -421,7 +422,10 @@ def test_block_mask_logical_skip_matches_oracle(case):
                                   ("tiny", dict(RAGGED, q_block=64), 0.2, 1.0),
                                   ("tiny", dict(RAGGED, num_q_heads=4), 0.5, 1.0),
                                   ("tiny", dict(RAGGED), 1.0, 0.9),
-                                  ("tiny_skip", {}, 0.5, 1.0)])
+                                  ("tiny_skip", {}, 0.5, 1.0),
+                                  # eight query heads per mask (four proxy rows each)
+                                  ("tiny", dict(RAGGED, num_q_heads=16, q_block=64), 0.3, 1.0),
+                                  ("tiny", dict(RAGGED, head_dim=64), 0.3, 1.0)])
 def test_kap_shared_kv_matches_oracle(case):
     name, kw, budget, top_p = case
     w, x = _inputs(name, **kw)
