@@ -49,6 +49,12 @@
 #ifndef COSA_HEAD_PAIRS
 #define COSA_HEAD_PAIRS 1
 #endif
+// Dense walk: the two heads of a workgroup in opposite phases (the products
+// of one head beside the softmax of the other); 0 selects the kernel whose
+// two heads run each page step together.
+#ifndef COSA_DENSE_PP
+#define COSA_DENSE_PP 1
+#endif
 
 namespace cosa {
 namespace {
@@ -862,6 +868,410 @@ attn_fwd_kernel(const AttnParams p) {
   }
 }
 
+// Dense walk with two query heads of a KV group per workgroup, the two heads
+// in opposite phases.  Wavefront w of head 0 and wavefront w of head 1 share
+// a SIMD (the waves of a workgroup go round-robin over the four SIMDs), so
+// when both heads run the same part of the page step at once, the matrix
+// core idles while both do the softmax on the VALU and the VALU idles while
+// both issue products.  Here each head's step is split into a product phase
+// M(t) = P V(t-1) then S(t) = K(t) Q^T (32 MFMAs per wavefront) and a vector
+// phase V(t) = mask, block max, rescale, P(t) = exp2(S(t) - mu) and its row
+// sum, and the heads take turns:
+//
+//     phase 2t     head 0: M(t)      head 1: V(t-1)
+//     phase 2t+1   head 0: V(t)      head 1: M(t)
+//
+// with one workgroup barrier per phase; the head in its product phase runs at
+// a raised wave priority, and only head 1 issues page copies, at the start of
+// its vector phases.  Each head still visits every causal block in ascending
+// order and applies the same arithmetic in the same order as the one-phase
+// step, so its output is the same bit for bit.  K(t) is read in phases 2t and
+// 2t+1 and V(t-1) in the same two, so after phase 2t+1 their LDS stages take
+// K(t+4) and V(t+3); the copies run three blocks ahead (four LDS stages per
+// operand, 128 KB, one workgroup per CU).
+template <int D>
+__global__ __launch_bounds__(512, 1) void attn_dense_pp_kernel(const AttnParams p) {
+  constexpr int NW = 4;                      // wavefronts per head, 32 query rows each
+  constexpr int NT = 2 * NW * 64;            // two heads
+  constexpr int BQ = NW * 32;                // query rows per tile
+  constexpr int NS = 4;                      // LDS stages per operand
+  constexpr int KCH = D / 8;                 // 16-byte chunks per key row
+  constexpr int K_TOTAL = kPage * KCH;       // 16-byte chunks per page
+  static_assert(K_TOTAL % NT == 0, "page copy must split evenly over the workgroup");
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  constexpr float kRescale = 8.f;
+  constexpr int kBytes = PageLayout<D>::kBytes;
+
+  __shared__ __attribute__((aligned(16))) unsigned char sK0[kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sK1[kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sK2[kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sK3[kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sV0[kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sV1[kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sV2[kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char sV3[kBytes];
+  __shared__ int sSlotP[2][64];   // [ring chunk][slot]: page of causal block
+  auto kbuf = [&](int x) -> unsigned char* {
+    return x == 0 ? sK0 : x == 1 ? sK1 : x == 2 ? sK2 : sK3;
+  };
+  auto vbuf = [&](int x) -> unsigned char* {
+    return x == 0 ? sV0 : x == 1 ? sV1 : x == 2 ? sV2 : sV3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / NW;                 // head of the workgroup (0 or 1)
+  const int wv = wave - grp * NW;
+  const int hf = lane >> 5;
+  const int col = lane & 31;
+
+  int b, hu, i;
+  decode_tile(p, blockIdx.x, p.hq / 2, b, hu, i);
+  const int h = hu * 2 + grp;
+  const int g = (hu * 2) / (p.hq / p.hkv);
+  const int q0 = p.cu_seqlens[b];
+  const int L = p.cu_seqlens[b + 1] - q0;
+  const int tile_q0 = i * BQ;
+  if (tile_q0 >= L) return;
+  const int tile_last = min(tile_q0 + BQ, L) - 1;
+  const int cnt = tile_last / kPage + 1;
+  const int32_t* __restrict__ pt = p.page_table + (int64_t)b * p.max_pages;
+
+  const int wave_q0 = tile_q0 + wv * 32;
+  const int wave_last = min(wave_q0 + 31, L - 1);
+  const int qpos = wave_q0 + col;
+  const bool row_valid = qpos < L;
+  const bool wave_has_rows = wave_q0 < L;
+
+  bf16x8_t qf[KSTEPS];
+  {
+    const uint16_t* qp = p.q + ((int64_t)(q0 + qpos) * p.hq + h) * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (row_valid) v = *reinterpret_cast<const u32x4_t*>(qp + ks * 16);
+      qf[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  // Page ids of the causal blocks from a two-chunk ring of 64 entries in LDS.
+  // Chunk c (slots 64c..) is copied into half c & 1 by the first copying
+  // wave at the start of block 64c - 6, before that block's page copies.
+  // Every wait for copies lets only the page copies of the two latest blocks
+  // stay in flight, so the chunk has landed by the first barrier of block
+  // 64c - 4 at the latest; slot 64c is first read in the second phase of that
+  // block.  The half's previous chunk (c - 2) was last read in block 64c - 68.
+  if (wave == 0) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int x = c * 64 + lane;
+      sSlotP[c][lane] = x < cnt ? pt[x] : 0;
+    }
+  }
+  __syncthreads();
+  auto slot_page = [&](int t) -> int { return sSlotP[(t >> 6) & 1][t & 63]; };
+
+  const int64_t head_stride = (int64_t)kPage * D;
+  const int64_t page_stride = (int64_t)p.hkv * head_stride;
+  // The page copies are issued by the wavefronts of head 1 only (K_PER
+  // copy instructions per page each), in the phase where that head runs its
+  // vector work, so the head issuing products never waits for room in the
+  // vector-memory queue.
+  constexpr int NC = NW * 64;                // copying threads
+  constexpr int K_PER = K_TOTAL / NC;
+  const int tidc = tid - NC;                 // valid for the copying threads
+  const int wavec = wave - NW;
+  uint32_t coff[K_PER];
+#pragma unroll
+  for (int e = 0; e < K_PER; ++e) {
+    const int f = e * NC + tidc;
+    const int r = f / KCH;
+    const int c = (f % KCH) ^ PageLayout<D>::swz(r);
+    coff[e] = (uint32_t)(r * D + c * 8) * 2u;
+  }
+  constexpr int kSliceBytes = kPage * D * 2;
+  auto copy_page = [&](const uint16_t* pool, int page, unsigned char* dst) __attribute__((always_inline)) {
+    const uint16_t* base = pool + (int64_t)page * page_stride + (int64_t)g * head_stride;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base), (short)0, kSliceBytes, kBufferWord3);
+#pragma unroll
+    for (int e = 0; e < K_PER; ++e) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(dst + (e * NC + wavec * 64) * 16), 16,
+          (int)coff[e], 0, 0, 0);
+    }
+  };
+
+  f32x16_t o[DBLK];
+#pragma unroll
+  for (int md = 0; md < DBLK; ++md) o[md] = (f32x16_t){};
+  float m_true = kNegInf;
+  float m_ref = kNegInf;
+  float lsum = 0.f;
+  const float c2 = p.scale_log2;
+
+  // S^T(block) = K Q^T for this wave's 32 queries, K operand reads two
+  // k-steps ahead of the products
+  auto qk = [&](const unsigned char* kb, f32x16_t (&sacc)[2]) __attribute__((always_inline)) {
+    constexpr int kAhead = 2;
+    u32x4_t a[kAhead + 1][2];
+    auto load = [&](int ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        a[ks % (kAhead + 1)][mb] = *reinterpret_cast<const u32x4_t*>(
+            kb + PageLayout<D>::offset(mb * 32 + col, 2 * ks + hf));
+    };
+#pragma unroll
+    for (int ks = 0; ks < kAhead; ++ks) load(ks);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if (ks + kAhead < KSTEPS) load(ks + kAhead);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, a[ks % (kAhead + 1)][mb]), qf[ks],
+            ks == 0 ? (f32x16_t){} : sacc[mb], 0, 0, 0);
+    }
+    // the first kAhead + 1 k-steps of reads, then one k-step of products
+    // and one of reads in turn, then the last products
+    __builtin_amdgcn_sched_group_barrier(0x100, (kAhead + 1) * 2, 0);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS - kAhead - 1; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, (kAhead + 1) * 2, 0);
+  };
+  int vtr[2][DBLK];
+  {
+    const int tr_row = 4 * hf + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row_r = 8 * r + tr_row;
+#pragma unroll
+      for (int md = 0; md < DBLK; ++md) {
+        const int colx = md * 32 + tr_col;
+        vtr[r][md] = PageLayout<D>::offset(row_r, colx >> 3) + ((colx & 7) << 1);
+      }
+    }
+  }
+  // O^T += V^T P^T (transposing LDS reads of the [key][D] page)
+  // V^T operand of product k = 4 ks + md (md < DBLK) of P V
+  auto pv_operand = [&](const unsigned char* vb, int k) __attribute__((always_inline)) -> u32x4_t {
+    const int ks = k / DBLK, md = k % DBLK;
+    u32x4_t a;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16_t*)(vb + vtr[r][md] + ks * (32 * D)));
+      const u32x2_t w = __builtin_bit_cast(u32x2_t, v);
+      a[2 * r] = w[0];
+      a[2 * r + 1] = w[1];
+    }
+    return a;
+  };
+  auto pv = [&](const unsigned char* vb, const bf16x8_t (&pb)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 4 * DBLK; ++k) {
+      const u32x4_t a = pv_operand(vb, k);
+      o[k % DBLK] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                            pb[k / DBLK], o[k % DBLK], 0, 0, 0);
+    }
+    // operand reads three products ahead
+    constexpr int kAhead = 3;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+    for (int k = 0; k < 4 * DBLK - kAhead; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+  };
+  // the vector phase of block s: causal / end mask, block max, online-softmax
+  // update with lazy rescaling, P(s) as the bf16 operand of P V and its row sum
+  auto vphase = [&](int s, f32x16_t (&sacc)[2], bf16x8_t (&pb)[4]) __attribute__((always_inline)) {
+    const int key0 = s * kPage;
+    if ((key0 + kPage - 1 > wave_q0) || (key0 + kPage > L)) {
+      const int lim = min(qpos, L - 1) - key0 - 4 * hf;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int koff = mb * 32 + 8 * (r >> 2) + (r & 3);
+          sacc[mb][r] = koff > lim ? kNegInf : sacc[mb][r];
+        }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
+    const float bm = pair_max(mx) * c2;
+    const float mn = fmaxf(m_true, bm);
+    m_true = mn;
+    const bool need = mn > m_ref + kRescale;
+    if (__any(need)) {
+      const float new_ref = need ? mn : m_ref;
+      const float alpha = (m_ref == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_ref - new_ref);
+      m_ref = new_ref;
+      lsum *= alpha;
+#pragma unroll
+      for (int md = 0; md < DBLK; ++md) o[md] *= alpha;
+    }
+    const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
+    float part = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mb][r], c2, -mu));
+        part += e;
+        pb[mb * 2 + (r >> 3)][r & 7] = (__bf16)e;
+      }
+    }
+    lsum += part;
+  };
+  // some key of block s is visible to some valid row of this wave
+  auto active = [&](int s) -> bool { return wave_has_rows && s * kPage <= wave_last; };
+
+  // prologue: K(0..2) and V(0..1); past the last block the copies repeat the
+  // last block's page into stages no step reads
+  if (grp == 1) {
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) copy_page(p.k_pool, pt[min(s, cnt - 1)], kbuf(s));
+#pragma unroll
+    for (int s = 0; s < NS - 2; ++s) copy_page(p.v_pool, pt[min(s, cnt - 1)], vbuf(s));
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  f32x16_t sacc[2];
+  bf16x8_t pb[4];
+  // pages of the copies the next block starts (uniform)
+  int nk = __builtin_amdgcn_readfirstlane(slot_page(min(NS - 1, cnt - 1)));
+  int nv = __builtin_amdgcn_readfirstlane(slot_page(min(NS - 2, cnt - 1)));
+
+  // One block: its two phases; stage of K(t) is t % NS, of V(t - 1) is
+  // (t - 1) % NS.  Each head runs its own copy of the loop (kB: head 1), so
+  // that the register allocation of each is its own; both pass the same
+  // barriers in the same order.
+  auto block = [&](const int t, auto stage_c, auto head_c) __attribute__((always_inline)) {
+    constexpr int sk = decltype(stage_c)::value;
+    constexpr int sv = (sk + NS - 1) % NS;
+    constexpr bool kB = decltype(head_c)::value;
+    // ---- phase 2t.  K(t) and V(t - 1) were copied three blocks ago; the
+    // copies of the two blocks since stay in flight.
+    if constexpr (kB) wait_vm_c<2 * 2 * K_PER>();
+    lds_barrier();
+    if (kB && wavec == 0 && ((t + 6) & 63) == 0 && t + 6 >= 128 && t + 6 < cnt) {
+      const int c = (t + 6) >> 6;
+      const int x = min(c * 64 + lane, cnt - 1);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(pt + x),
+                                       (__attribute__((address_space(3))) void*)&sSlotP[c & 1][0],
+                                       4, 0, 0);
+    }
+    // K(t + 3) into the stage of K(t - 1), V(t + 2) into that of V(t - 2)
+    if constexpr (kB) {
+      copy_page(p.k_pool, nk, kbuf((sk + NS - 1) % NS));
+      copy_page(p.v_pool, nv, vbuf((sk + 2) % NS));
+    }
+    const bool pv_on = t > 0 && active(t - 1);
+    const bool qk_on = active(t);
+    // the head issuing products takes issue priority over the other
+    if constexpr (!kB) {
+      __builtin_amdgcn_s_setprio(1);
+      if (pv_on) pv(vbuf(sv), pb);
+      if (qk_on) qk(kbuf(sk), sacc);
+      __builtin_amdgcn_s_setprio(0);
+    } else {
+      if (pv_on) vphase(t - 1, sacc, pb);
+    }
+    // ---- phase 2t + 1
+    lds_barrier();
+    const int rk = slot_page(min(t + NS, cnt - 1));
+    const int rv = slot_page(min(t + NS - 1, cnt - 1));
+    if constexpr (!kB) {
+      if (qk_on) vphase(t, sacc, pb);
+    } else {
+      __builtin_amdgcn_s_setprio(1);
+      if (pv_on) pv(vbuf(sv), pb);
+      if (qk_on) qk(kbuf(sk), sacc);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    nk = __builtin_amdgcn_readfirstlane(rk);
+    nv = __builtin_amdgcn_readfirstlane(rv);
+  };
+  auto run = [&](auto head_c) __attribute__((always_inline)) {
+    constexpr bool kB = decltype(head_c)::value;
+    int t0 = 0;
+    for (; t0 + NS <= cnt; t0 += NS) {
+      block(t0, std::integral_constant<int, 0>{}, head_c);
+      block(t0 + 1, std::integral_constant<int, 1>{}, head_c);
+      block(t0 + 2, std::integral_constant<int, 2>{}, head_c);
+      block(t0 + 3, std::integral_constant<int, 3>{}, head_c);
+    }
+    if (t0 < cnt) block(t0, std::integral_constant<int, 0>{}, head_c);
+    if (t0 + 1 < cnt) block(t0 + 1, std::integral_constant<int, 1>{}, head_c);
+    if (t0 + 2 < cnt) block(t0 + 2, std::integral_constant<int, 2>{}, head_c);
+
+    // ---- drain: P V of the last block, after its V page's tail past the
+    // end of the sequence (P is 0 there, 0 * NaN is not) is zeroed
+    const int last = cnt - 1;
+    unsigned char* vl = vbuf(last & (NS - 1));
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    if (last * kPage + kPage > L) {
+      const int valid = L - last * kPage;
+      for (int f = valid * KCH + tid; f < kPage * KCH; f += NT)
+        *reinterpret_cast<u32x4_t*>(vl + f * 16) = (u32x4_t){0u, 0u, 0u, 0u};
+      lds_barrier();
+    }
+    const bool last_on = active(last);
+    if constexpr (!kB) {
+      if (last_on) pv(vl, pb);
+      lds_barrier();
+    } else {
+      if (last_on) vphase(last, sacc, pb);
+      lds_barrier();
+      if (last_on) pv(vl, pb);
+    }
+  };
+  if (grp == 0)
+    run(std::false_type{});
+  else
+    run(std::true_type{});
+
+  // ---- epilogue: out = O / l, lse = m + ln l
+  const float ltot = pair_sum(lsum);
+  if (row_valid) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    uint16_t* dst = p.out + ((int64_t)(q0 + qpos) * p.hq + h) * D;
+#pragma unroll
+    for (int md = 0; md < DBLK; ++md) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d = md * 32 + 8 * rq + 4 * hf;
+        __bf16 v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[md][4 * rq + e] * inv);
+        u32x2_t w;
+        w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v4[0]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, v4[1]) << 16);
+        w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v4[2]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, v4[3]) << 16);
+        *reinterpret_cast<u32x2_t*>(dst + d) = w;
+      }
+    }
+    if (p.lse != nullptr && hf == 0) {
+      p.lse[(int64_t)h * p.total_q + q0 + qpos] =
+          ltot > 0.f ? (m_ref + __log2f(ltot)) * kLn2 : kNegInf;
+    }
+  }
+}
+
 template <int D, int NW, int kMode, int PPB, int HP, int NS>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const int64_t n_groups = p.group_count > 0 ? p.group_count : (int64_t)p.batch * p.hkv;
@@ -888,7 +1298,15 @@ hipError_t launch_mode(const AttnParams& p, AttnMode mode, int ppb, hipStream_t 
 // Two query heads per workgroup for the dense walk (every head of a KV group
 // visits the same pages), four LDS stages.
 hipError_t launch_dense_pairs(const AttnParams& p, hipStream_t stream) {
+#if COSA_DENSE_PP
+  const int64_t n_groups = p.group_count > 0 ? p.group_count : (int64_t)p.batch * p.hkv;
+  const int64_t grid = n_groups * (p.hq / p.hkv / 2) * p.nqb;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_dense_pp_kernel<128>, dim3((unsigned)grid), dim3(512), 0, stream, p);
+  return hipGetLastError();
+#else
   return launch_one<128, 4, kModeDense, 1, 2, 4>(p, stream);
+#endif
 }
 
 }  // namespace
