@@ -163,6 +163,37 @@ def test_osk_full_budget_skip_off_equals_dense(case):
     _run_osk_vs_oracle(w, x, blocks, counts, -1.0, f"osk-full {name}")
 
 
+@pytest.mark.parametrize("seqlens", [RAGGED["seqlens"], (9000, 20000, 130)])
+def test_osk_every_block_ascending_equals_dense_bitwise(seqlens):
+    # The ordered walk over every causal block in ascending order with the skip
+    # off visits what the dense walk visits, in the same order, with the same
+    # arithmetic: the outputs and LSE agree bit for bit (the dense kernel pairs
+    # two query heads per workgroup in opposite phases; the ordered kernel runs
+    # one head per workgroup).  The longer sequences refill the slot rings.
+    w, x = _inputs("tiny", **dict(RAGGED, seqlens=seqlens, num_q_heads=4, num_kv_heads=2))
+    print(f"[case] osk ascending every block vs dense, seqlens={seqlens}", flush=True)
+    prob, q, k, v = upload(x, DEV)
+    blocks, counts = oosk.dense_order_mask(x.cu_seqlens, w.num_q_heads, w.q_block, w.block)
+    C = blocks.shape[-1]
+    pages = np.full(blocks.shape, -1, dtype=np.int32)
+    for b in range(w.batch):
+        for idx in np.ndindex(*blocks.shape[1:-1]):
+            row = blocks[(b,) + idx]
+            n_ = int((row >= 0).sum())
+            pages[(b,) + idx][:n_] = x.page_table[b][row[:n_]]
+    mask = bk.OrderedMask(blocks=torch.from_numpy(blocks).to(DEV),
+                          pages=torch.from_numpy(pages).to(DEV),
+                          counts=torch.from_numpy(counts).to(DEV), hrm_counts=None, capacity=C)
+    o = bk.osk_prefill(prob, q, k, v, mask, -1.0)
+    d = bk.dense_prefill(prob, q, k, v)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(d.out.float()).any())
+    assert torch.equal(o.out, d.out)
+    assert torch.equal(o.lse, d.lse)
+    report(f"osk ascending = dense {seqlens}", tiles=int((counts > 0).sum()),
+           max_blocks=int(counts.max()))
+
+
 @pytest.mark.parametrize("tau", [-1.0, 0.0, 4.0, 8.0])
 def test_osk_oracle_mask_with_skip(tau):
     w, x = _inputs("tiny_skip")
