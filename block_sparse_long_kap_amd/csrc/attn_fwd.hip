@@ -1287,7 +1287,6 @@ template <int D, int NW>
 hipError_t launch_mode(const AttnParams& p, AttnMode mode, int ppb, hipStream_t stream) {
   if (ppb == 2) {
     if (mode == kModeOrdered) return launch_one<D, NW, kModeOrdered, 2, 1, 2>(p, stream);
-    if (mode == kModeDense) return launch_one<D, NW, kModeDense, 2, 1, 2>(p, stream);
     return hipErrorInvalidValue;
   }
   if (mode == kModeOrdered) return launch_one<D, NW, kModeOrdered, 1, 1, 2>(p, stream);
@@ -1316,13 +1315,16 @@ hipError_t launch_attention(const AttnParams& p, int head_dim, int q_block, Attn
   // a range of groups is only defined in the group-major order
   if (p.group_count > 0 && p.order != kOrderGroupMajor && p.order != kOrderGroupXcd)
     return hipErrorInvalidValue;
-  if (COSA_HEAD_PAIRS && mode == kModeDense && p.ppb == 1 && head_dim == 128 &&
-      q_block == 128 && (p.hq / p.hkv) % 2 == 0)
+  // The dense walk visits every causal key in ascending order whatever the
+  // logical block size, so it walks one 64-key page per step.
+  const int ppb = mode == kModeDense ? 1 : p.ppb;
+  if (COSA_HEAD_PAIRS && mode == kModeDense && head_dim == 128 && q_block == 128 &&
+      (p.hq / p.hkv) % 2 == 0)
     return launch_dense_pairs(p, stream);
-  if (head_dim == 128 && q_block == 128) return launch_mode<128, 4>(p, mode, p.ppb, stream);
-  if (head_dim == 128 && q_block == 64) return launch_mode<128, 2>(p, mode, p.ppb, stream);
-  if (head_dim == 64 && q_block == 128) return launch_mode<64, 4>(p, mode, p.ppb, stream);
-  if (head_dim == 64 && q_block == 64) return launch_mode<64, 2>(p, mode, p.ppb, stream);
+  if (head_dim == 128 && q_block == 128) return launch_mode<128, 4>(p, mode, ppb, stream);
+  if (head_dim == 128 && q_block == 64) return launch_mode<128, 2>(p, mode, ppb, stream);
+  if (head_dim == 64 && q_block == 128) return launch_mode<64, 4>(p, mode, ppb, stream);
+  if (head_dim == 64 && q_block == 64) return launch_mode<64, 2>(p, mode, ppb, stream);
   return hipErrorInvalidValue;
 }
 

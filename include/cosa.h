@@ -348,9 +348,10 @@ cosa_status cosa_osk_prefill_delta(const cosa_problem* p, const void* q, const v
                                    uint8_t* skip_record, int32_t* row_stats, void* stream);
 
 /*
- * Dense causal prefill on the same kernel: every tile visits all of its
- * causal key blocks j = 0 .. (last row) / kv_block in ascending order through
- * page_table, with no in-kernel skip (CoSA (paperpeel) §3.1, FlashAttention-2
+ * Dense causal prefill on the same page step: every tile visits all of its
+ * causal keys in ascending order through page_table, one page_size-key page at
+ * a time whatever kv_block is (the result does not depend on the logical block
+ * size), with no in-kernel skip (CoSA (paperpeel) §3.1, FlashAttention-2
  * baseline of §5.1).  out / lse as for cosa_osk_prefill().
  */
 cosa_status cosa_dense_prefill(const cosa_problem* p, const void* q, const void* k_pool,
