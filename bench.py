@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 TRAFFIC_PROFILE = "profiles/attn_kap_llama128k_hbm_traffic.md"
+COUNTERS_PROFILE = "profiles/attn_kap_llama128k_counters.md"
 # (Top-p, Delta) operating points of the pages: Qwen3-8B uses p = 0.95 with
 # Delta = 2000 (1000 for the accuracy-first variant), Llama-3.1-8B Delta = 200
 TOP_P_DELTA_POINTS = [(0.95, 2000.0), (0.95, 1000.0), (0.95, 200.0), (0.9, 200.0)]
@@ -247,6 +248,15 @@ def main():
     # only while it was taken on the current kernel sources and settings
     # (not measured in this run; null once the kernel has changed)
     traffic = profsum.read_traffic(os.path.join(ROOT, TRAFFIC_PROFILE), w.name, budget, tau)
+    # the matrix cores' busy share (SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs'
+    # GRBM_GUI_ACTIVE cycles) of the OSK and dense launches, likewise from the
+    # committed counter summary while it matches the kernel sources
+    osk_util = profsum.read_mfma_util(os.path.join(ROOT, COUNTERS_PROFILE), w.name, budget, tau,
+                                      "cosa_osk_prefill")
+    dense_util = profsum.read_mfma_util(os.path.join(ROOT, COUNTERS_PROFILE), w.name, budget,
+                                        tau, "cosa_dense_prefill")
+    util_source = (COUNTERS_PROFILE + " (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES, "
+                   "GRBM_GUI_ACTIVE on the same kernel sources; not measured in this run)")
     kap_bytes = (q.numel() * 2 + (w.total_tokens * w.num_kv_heads * w.head_dim * 2)
                  + 2 * mask.blocks.numel() * 4 + mask.counts.numel() * 8)
     result = {
@@ -277,6 +287,8 @@ def main():
         "dense_tflops": None if dense_ms is None else round(dense_flops / dense_ms / 1e9, 1),
         "dense_mfma_frac": None if dense_ms is None else
         round(dense_flops / dense_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+        "dense_mfma_util": None if dense_ms is None or dense_util is None else
+        dense_util["mfma_util"],
         "osk_tflops": round(osk_tflops, 1),
         "osk_mfma_frac": round(osk_tflops / PEAK_BF16_TFLOPS, 4),
         "kap_gbs": round(kap_bytes / (kap_ms * 1e-3) / 1e9, 1),
@@ -298,6 +310,8 @@ def main():
                      "traffic_source": None if traffic is None else
                      TRAFFIC_PROFILE + " (rocprofv3 --pmc on the same kernel sources; "
                      "not measured in this run)",
+                     "mfma_util": None if osk_util is None else osk_util["mfma_util"],
+                     "mfma_util_source": None if osk_util is None else util_source,
                      "kernel": "attn_fwd_kernel<128, 4, 1, 1, 1, 2> (cosa_osk_prefill)",
                      "launch_ms": round(osk_ms, 4),
                      "algorithmic_flop_per_launch": osk_flops,

@@ -7,13 +7,15 @@ Usage (after the rocprofv3 runs named in each mode's docstring)::
     python3 profsum.py traffic  FETCH.csv WRITE.csv COPY_FETCH.csv \
         COPY_WRITE.csv --copy-bytes 1073741824 --workload llama128k --budget 0.1 --tau 8 \
         --command "..."
-    python3 profsum.py counters COUNTERS.csv --command "..."
+    python3 profsum.py counters COUNTERS.csv --command "..." \
+        [--workload llama128k --budget 0.1 --tau 8]
 
 Each mode prints Markdown.  The traffic mode also prints one
 ``bench-traffic: {json}`` line per attention kernel, which ``bench.py`` reads
-back to fill the roofline's ``traffic`` field, but only while the digest of
-the attention kernel's sources still matches the one recorded with the
-counters (a changed kernel invalidates them).
+back to fill the roofline's ``traffic`` field, and the counters mode with a
+workload one ``bench-mfma: {json}`` line per attention kernel (its MfmaUtil),
+both only while the digest of the attention kernel's sources still matches
+the one recorded with the counters (a changed kernel invalidates them).
 """
 from __future__ import annotations
 
@@ -56,6 +58,8 @@ def attention_source_digest(read=None) -> str:
 def entry_of(kernel: str):
     """C entry point that launches an attention kernel instance, from the last
     template argument (the page-walk mode), or None for other kernels."""
+    if re.search(r"attn_dense_pp_kernel<", kernel):
+        return "cosa_dense_prefill"
     m = re.search(r"attn_fwd_kernel<\s*\d+,\s*\d+,\s*(\w+)\s*(?:,\s*\d+\s*)*>", kernel)
     if not m:
         return None
@@ -172,8 +176,14 @@ def traffic_md(fetch, write, cfetch, cwrite, copy_bytes, workload, budget, tau, 
     return "\n".join(lines)
 
 
-def counters_md(path, command, xcds=8, simds=1024):
+def counters_md(path, command, xcds=8, simds=1024, workload=None, budget=None, tau=None):
+    """Per-dispatch means per (kernel, grid size) and the MfmaUtil of each
+    where the pass holds its counters; with a workload, one ``bench-mfma``
+    line per attention kernel, which bench.py reads back while the attention
+    sources still match the recorded digest."""
     agg = per_kernel_counter(path)
+    records = []
+    digest = attention_source_digest() if workload is not None else None
     kernels = sorted({kw for kw, _ in agg if "cosa" in kw[0]},
                      key=lambda kw: (kw[0], -(kw[1] or 0)))
     names = sorted({c for _, c in agg})
@@ -185,11 +195,40 @@ def counters_md(path, command, xcds=8, simds=1024):
         util = ""
         if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and vals.get("GRBM_GUI_ACTIVE"):
             # GRBM_GUI_ACTIVE is summed over the XCDs; busy cycles over the SIMDs
-            util = f"{vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (vals['GRBM_GUI_ACTIVE'] / xcds * simds):.3f}"
+            u = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (vals["GRBM_GUI_ACTIVE"] / xcds * simds)
+            util = f"{u:.3f}"
+            if workload is not None and entry_of(k[0]) is not None:
+                records.append({"kernel": short_name(k[0]), "entry": entry_of(k[0]),
+                                "workgroups": k[1], "workload": workload, "budget": budget,
+                                "tau": tau, "mfma_util": round(u, 4), "source_digest": digest})
         out.append(f"| `{short_name(k[0])}` | {k[1]} | " +
                    " | ".join(f"{vals[c]:.4g}" if c in vals else "" for c in names) +
                    f" | {util} |")
+    if records:
+        out.append("")
+        out += ["bench-mfma: " + json.dumps(r) for r in records]
     return "\n".join(out)
+
+
+def read_mfma_util(path, workload, budget, tau, entry):
+    """MfmaUtil recorded for the whole-layer launch (largest grid) of the kernel
+    behind ``entry`` with these settings, or None when absent or taken on
+    different kernel sources."""
+    if not os.path.exists(path):
+        return None
+    digest = attention_source_digest()
+    best = None
+    with open(path) as f:
+        for line in f:
+            if not line.startswith("bench-mfma: "):
+                continue
+            r = json.loads(line[len("bench-mfma: "):])
+            if (r.get("entry") == entry and r["workload"] == workload and
+                    abs(r["budget"] - budget) < 1e-9 and abs(r["tau"] - tau) < 1e-9 and
+                    r["source_digest"] == digest):
+                if best is None or (r.get("workgroups") or 0) > (best.get("workgroups") or 0):
+                    best = r
+    return best
 
 
 def read_traffic(path, workload, budget, tau):
@@ -235,6 +274,9 @@ def main(argv=None):
     c = sub.add_parser("counters")
     c.add_argument("csv")
     c.add_argument("--command", required=True)
+    c.add_argument("--workload")
+    c.add_argument("--budget", type=float)
+    c.add_argument("--tau", type=float)
     a = ap.parse_args(argv)
     if a.mode == "stats":
         print(stats_md(a.csv, a.command))
@@ -244,7 +286,7 @@ def main(argv=None):
         print(traffic_md(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes, a.workload,
                          a.budget, a.tau, a.command))
     else:
-        print(counters_md(a.csv, a.command))
+        print(counters_md(a.csv, a.command, workload=a.workload, budget=a.budget, tau=a.tau))
     return 0
 
 

@@ -104,3 +104,31 @@ def test_traffic_keeps_launch_sizes_apart(tmp_path):
     r = profsum.read_traffic(str(prof), "wl", 0.1, 8.0)
     assert r["workgroups"] == 8
     assert r["read_bytes"] == 1600 * 1024 and r["write_bytes"] == 80 * 1024
+
+
+def test_mfma_util_lines_and_readback(tmp_path):
+    osk = "void cosa::(anonymous namespace)::attn_fwd_kernel<128, 4, 1, 1, 1, 2>(cosa::AttnParams)"
+    dense = "void cosa::(anonymous namespace)::attn_dense_pp_kernel<128>(cosa::AttnParams)"
+    kap = "void cosa::(anonymous namespace)::kap_select<128, 8, false, 1>(cosa::KapParams)"
+    p = tmp_path / "c.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Name", "Counter_Value"])
+        # whole-layer OSK launch (8 workgroups) and a chunk launch (1 workgroup)
+        for name, grid, busy, active in [(osk, 2048, 4096.0, 64.0), (osk, 256, 1024.0, 64.0),
+                                         (dense, 4096, 6144.0, 64.0), (kap, 256, 512.0, 64.0)]:
+            w.writerow([name, grid, 256, "SQ_VALU_MFMA_BUSY_CYCLES", busy])
+            w.writerow([name, grid, 256, "GRBM_GUI_ACTIVE", active])
+    md = profsum.counters_md(str(p), "cmd", xcds=8, simds=64, workload="wl", budget=0.1, tau=8.0)
+    prof = tmp_path / "p.md"
+    prof.write_text(md)
+    # util = busy / (active / 8 XCDs x 64 SIMDs) = busy / 512
+    r = profsum.read_mfma_util(str(prof), "wl", 0.1, 8.0, "cosa_osk_prefill")
+    assert r["workgroups"] == 8 and r["mfma_util"] == 8.0
+    assert profsum.read_mfma_util(str(prof), "wl", 0.1, 8.0, "cosa_dense_prefill")["mfma_util"] == 12.0
+    assert profsum.read_mfma_util(str(prof), "wl", 0.2, 8.0, "cosa_osk_prefill") is None
+    assert not any("kap_select" in l for l in md.splitlines() if l.startswith("bench-mfma"))
+    prof.write_text(md.replace(profsum.attention_source_digest(), "0" * 16))
+    assert profsum.read_mfma_util(str(prof), "wl", 0.1, 8.0, "cosa_osk_prefill") is None
+    # without a workload no readback lines are written
+    assert "bench-mfma" not in profsum.counters_md(str(p), "cmd")
