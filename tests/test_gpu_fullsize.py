@@ -334,6 +334,44 @@ def test_long_tile_skip_parity(case):
     sl.assert_ok(max_abs=1e-3, mean_abs=1e-4, label=f"long-tile {name} osk lse")
 
 
+def test_llama128k_every_block_ascending_equals_dense_bitwise():
+    """The benchmark layer (llama128k) with every causal block of every tile
+    in ascending order and the skip off: the ordered kernel then visits what
+    the dense kernel visits, in the same order, with the same arithmetic, and
+    the two agree bit for bit on every output and LSE value (1.07e9 + 4.2e6)."""
+    w = ci.get("llama128k")
+    print("[case] llama128k every block ascending vs dense: inputs", flush=True)
+    x = ci.make(w).bf16_rounded()
+    prob, q, k, v = upload(x, DEV)
+    L = int(x.cu_seqlens[1])
+    nqb = (L + w.q_block - 1) // w.q_block
+    C = (L + w.page_size - 1) // w.page_size
+    n_i = (torch.minimum((torch.arange(nqb, device=DEV) + 1) * w.q_block,
+                         torch.tensor(L, device=DEV)) - 1) // w.page_size + 1
+    ar = torch.arange(C, device=DEV, dtype=torch.int32)
+    valid = ar[None, :] < n_i[:, None]                              # [nqb][C]
+    blocks = torch.where(valid, ar[None, :], torch.tensor(-1, device=DEV, dtype=torch.int32))
+    pt = torch.from_numpy(x.page_table[0].astype(np.int32)).to(DEV)
+    pages = torch.where(valid, pt[ar.long()][None, :], torch.tensor(-1, device=DEV,
+                                                                    dtype=torch.int32))
+    shape = (1, w.num_q_heads, nqb, C)
+    mask = bk.OrderedMask(blocks=blocks[None, None].expand(shape).contiguous(),
+                          pages=pages[None, None].expand(shape).contiguous(),
+                          counts=n_i.to(torch.int32)[None, None].expand(shape[:3]).contiguous(),
+                          hrm_counts=None, capacity=C)
+    print("[case] llama128k every block ascending vs dense: GPU layer", flush=True)
+    o = bk.osk_prefill(prob, q, k, v, mask, -1.0)
+    d = bk.dense_prefill(prob, q, k, v)
+    torch.cuda.synchronize()
+    assert int(o.row_stats[..., 1].sum()) == 0
+    assert bool(torch.isfinite(d.out.float()).all())
+    same_out = torch.equal(o.out, d.out)
+    same_lse = torch.equal(o.lse, d.lse)
+    report("llama128k ascending = dense", out_equal=same_out, lse_equal=same_lse,
+           slots=int(n_i.sum()) * w.num_q_heads)
+    assert same_out and same_lse
+
+
 def test_stress_full_budget_skip_off_equals_dense():
     """The stress batch (16K + 48K + 96K + 128K in one pool) at a 100% stage-1
     budget with the in-kernel skip off (tau < 0, Delta = -1 of App. D.1): the
