@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--shared-kv", action="store_true",
                     help="also time the KAP + OSK with one mask per KV head shared by its query "
                          "heads (extra JSON line)")
+    ap.add_argument("--lengths", action="store_true",
+                    help="also time the sparse layer and the dense kernel at 4K ... 128K tokens "
+                         "(one sequence, the workload's shape and structure; extra JSON lines)")
     ap.add_argument("--only", choices=["all", "kap", "osk", "dense"], default="all",
                     help="launch only one kernel kind (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -363,6 +366,9 @@ def main():
         shared_kv_bench(args, w, bk, prob, q, kp, vp, ws, out, stream, ev, causal_slots, fps,
                         budget, tau, dense_ms)
 
+    if args.lengths and args.only == "all":
+        length_sweep(args, w, bk, torch, dev, stream, ev, budget, tau, (x, q, kp, vp))
+
     if args.logical_skip:
         logical_skip_bench(args, w, bk, prob, q, kp, vp, ws, out, stream, ev, causal_slots,
                            dense_ms)
@@ -552,6 +558,83 @@ def shared_kv_bench(args, w, bk, prob, q, kp, vp, ws, out, stream, ev, causal_sl
                       "stage1_budget": round(vis / causal_slots, 5),
                       "skip_ratio": round(skp / max(vis, 1), 5),
                       "osk_tflops": round(fps * (2 * vis - skp) / om / 1e9, 1)}), flush=True)
+
+
+SWEEP_LENGTHS = (4096, 8192, 16384, 32768, 65536, 131072)
+
+
+def length_sweep(args, w, bk, torch, dev, stream, ev, budget, tau, headline):
+    """The layer at growing context lengths (one sequence of N tokens, the
+    workload's head shape, planted structure, budget and tau): the fused
+    sparse call, its two halves as separate calls, and the dense kernel on
+    the same inputs, one JSON line per length.  ``headline`` holds the
+    workload's own (x, q, k_pool, v_pool), reused at its length."""
+    import cosa_inputs as ci
+    side = torch.cuda.Stream(dev)
+    for n in SWEEP_LENGTHS:
+        if n > w.max_seqlen:
+            continue
+        wn = w.with_(name=f"{w.name}@{n}", seqlens=(n,))
+        if n == w.max_seqlen and w.batch == 1:
+            x, q, kp, vp = headline
+        else:
+            x = ci.make(wn)
+            q = torch.from_numpy(x.q).to(torch.bfloat16).to(dev)
+            kp = torch.from_numpy(x.k_pool).to(torch.bfloat16).to(dev)
+            vp = torch.from_numpy(x.v_pool).to(torch.bfloat16).to(dev)
+        prob = bk.Problem(cu_seqlens=torch.from_numpy(x.cu_seqlens).to(dev),
+                          page_table=torch.from_numpy(x.page_table).to(dev),
+                          num_q_heads=wn.num_q_heads, num_kv_heads=wn.num_kv_heads,
+                          head_dim=wn.head_dim, max_seqlen=n, total_q=n,
+                          num_pages=x.k_pool.shape[0], q_block=wn.q_block,
+                          page_size=wn.page_size, kv_block=wn.block,
+                          softmax_scale=wn.softmax_scale)
+        ws = bk.KapWorkspace(prob)
+        mask, res = bk.sparse_prefill(prob, q, kp, vp, budget, tau, aux_stream=side,
+                                      workspace=ws)
+        dout = bk.dense_prefill(prob, q, kp, vp)
+        torch.cuda.synchronize()
+        st = res.row_stats.cpu().numpy().reshape(-1, 2)
+        vis, skp = int(st[:, 0].sum()), int(st[:, 1].sum())
+        causal = wn.num_q_heads * sum((min((i + 1) * wn.q_block, n) - 1) // wn.block + 1
+                                      for i in range(-(-n // wn.q_block)))
+
+        def fused():
+            bk.sparse_prefill(prob, q, kp, vp, budget, tau, aux_stream=side, workspace=ws,
+                              mask=mask, out=res)
+
+        for _ in range(max(1, args.warmup)):
+            fused()
+            bk.dense_prefill(prob, q, kp, vp, out=dout)
+        torch.cuda.synchronize()
+        e = [ev() for _ in range(5)]
+        e[0].record(stream)
+        for _ in range(args.steps):
+            fused()
+        e[1].record(stream)
+        for _ in range(args.steps):
+            bk.proxy_ordered_mask(prob, q, kp, budget, workspace=ws, out=mask)
+        e[2].record(stream)
+        for _ in range(args.steps):
+            bk.osk_prefill(prob, q, kp, vp, mask, tau, out=res)
+        e[3].record(stream)
+        nd = max(2, args.steps // 2)
+        for _ in range(nd):
+            bk.dense_prefill(prob, q, kp, vp, out=dout)
+        e[4].record(stream)
+        torch.cuda.synchronize()
+        sm = e[0].elapsed_time(e[1]) / args.steps
+        km = e[1].elapsed_time(e[2]) / args.steps
+        om = e[2].elapsed_time(e[3]) / args.steps
+        dm = e[3].elapsed_time(e[4]) / nd
+        print(json.dumps({"length_sweep": w.name, "seqlen": n, "budget": budget, "tau": tau,
+                          "ms_per_layer": round(sm, 4), "kap_ms": round(km, 4),
+                          "osk_ms": round(om, 4), "dense_ms": round(dm, 4),
+                          "speedup_vs_dense": round(dm / sm, 3),
+                          "kap_share": round(km / (km + om), 4),
+                          "stage1_budget": round(vis / causal, 5),
+                          "skip_ratio": round(skp / max(vis, 1), 5)}), flush=True)
+        del mask, res, dout, ws
 
 
 LOGICAL_SKIP_BUDGETS = (0.5, 0.3, 0.2, 0.1, 0.05)

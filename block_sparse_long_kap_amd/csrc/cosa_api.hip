@@ -432,9 +432,18 @@ COSA_EXPORT cosa_status cosa_sparse_prefill(
   hipError_t e = cosa::launch_kap(k, p->head_dim, p->q_block, s0, cosa::kKapPool);
   if (e != hipSuccess) return hip_status(e);
   // (sequence, KV head) groups in at most 8 chunks: the proxy of chunk c+1
-  // runs while the kernel of chunk c does
+  // runs while the kernel of chunk c does.  Each chunk's kernel spans at
+  // least kChunkWorkgroups workgroups (eight rounds of two per CU), or the
+  // launch gaps, the stream hand-offs and the tail of every launch cost more
+  // than the hidden proxy time wins: shorter inputs take fewer, larger
+  // chunks, down to one on the caller's stream.
+  constexpr int64_t kChunkWorkgroups = 4096;
   const int n_groups = p->batch * p->num_kv_heads;
-  const int chunk = (n_groups + 7) / 8;
+  const int64_t wg_per_group = (int64_t)(p->num_q_heads / p->num_kv_heads) * a.nqb;
+  int chunk = (n_groups + 7) / 8;
+  const int64_t need = (kChunkWorkgroups + wg_per_group - 1) / wg_per_group;
+  if (need > chunk) chunk = need < n_groups ? (int)need : n_groups;
+  const bool overlap = s1 != nullptr && chunk < n_groups;
   hipEvent_t ev[9] = {};
   int n_ev = 0;
   auto cleanup = [&]() {
@@ -450,7 +459,7 @@ COSA_EXPORT cosa_status cosa_sparse_prefill(
     e = cosa::launch_kap(k, p->head_dim, p->q_block, s0, cosa::kKapSelect);
     if (e != hipSuccess) break;
     hipStream_t s_attn = s0;
-    if (s1 != nullptr) {
+    if (overlap) {
       e = hipEventCreateWithFlags(&ev[n_ev], hipEventDisableTiming);
       if (e != hipSuccess) break;
       ++n_ev;

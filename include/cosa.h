@@ -296,13 +296,14 @@ cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, const void* k
  * attention to out / lse / skip_record / row_stats, with the layouts given
  * there.
  *
- * The work is cut into at most 8 chunks of (sequence, KV head) groups; the
- * proxy of every chunk runs on `stream`.  With aux_stream != NULL (another
- * stream of the same device, not `stream`), the kernel of chunk c runs on
- * aux_stream after the proxy of chunk c, so that the proxy of later chunks
- * overlaps it, and `stream` waits for the last kernel before the call's
- * later work; with aux_stream == NULL everything runs on `stream` in chunk
- * order.  Argument errors (including the proxy's 2048-key-block limit) as
+ * The work is cut into at most 8 chunks of (sequence, KV head) groups, each
+ * chunk's kernel at least 4096 workgroups (query heads x query tiles) where
+ * the groups allow, so short inputs run as one chunk; the proxy of every
+ * chunk runs on `stream`.  With aux_stream != NULL (another stream of the
+ * same device, not `stream`) and more than one chunk, the kernel of chunk c
+ * runs on aux_stream after the proxy of chunk c, so that the proxy of later
+ * chunks overlaps it, and `stream` waits for the last kernel before the
+ * call's later work; otherwise everything runs on `stream` in chunk order.  Argument errors (including the proxy's 2048-key-block limit) as
  * for the two calls; COSA_ERR_HIP if an event cannot be created.  The call
  * allocates no device memory.
  */

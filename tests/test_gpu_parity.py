@@ -604,8 +604,11 @@ def test_empty_sequences_and_single_block_budget():
 
 @pytest.mark.parametrize("case", [
     ("tiny_skip", {}, 0.5, 2.0),
-    # 6 sequences x 2 KV heads = 12 groups: chunks of 2 groups, the last ones empty
+    # 6 sequences x 2 KV heads = 12 groups, one chunk at this size
     ("tiny", dict(RAGGED, q_dir_gain=6.0), 0.2, 2.0),
+    # 4 sequences x 8 KV heads = 32 groups of 2048 workgroups (64K tokens): eight
+    # chunks of 4 groups, two of them on the empty sequence; the skip fires
+    ("remap32k", dict(seqlens=(65536, 0, 3000, 40000)), 0.3, 6.0),
     ("tiny", dict(RAGGED, seqlens=(1500, 0, 700, 2047), num_kv_heads=4), 0.3, -1.0),
     # 128-key logical blocks over two pages
     ("tiny_skip", dict(kv_block=128), 0.5, 2.0),
