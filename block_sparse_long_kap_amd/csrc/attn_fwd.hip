@@ -882,8 +882,8 @@ attn_fwd_kernel(const AttnParams p) {
 //     phase 2t+1   head 0: V(t)      head 1: M(t)
 //
 // with one workgroup barrier per phase; the head in its product phase runs at
-// a raised wave priority, and only head 1 issues page copies, at the start of
-// its vector phases.  Each head still visits every causal block in ascending
+// a raised wave priority, and the page copies are issued at the start of the
+// vector phases, the K pages by head 1 and the V pages by head 0.  Each head still visits every causal block in ascending
 // order and applies the same arithmetic in the same order as the one-phase
 // step, so its output is the same bit for bit.  K(t) is read in phases 2t and
 // 2t+1 and V(t-1) in the same two, so after phase 2t+1 their LDS stages take
@@ -957,8 +957,8 @@ __global__ __launch_bounds__(512, 1) void attn_dense_pp_kernel(const AttnParams 
   }
 
   // Page ids of the causal blocks from a two-chunk ring of 64 entries in LDS.
-  // Chunk c (slots 64c..) is copied into half c & 1 by the first copying
-  // wave at the start of block 64c - 6, before that block's page copies.
+  // Chunk c (slots 64c..) is copied into half c & 1 by the first wavefront
+  // of head 1 at the start of block 64c - 6, before that block's K copies.
   // Every wait for copies lets only the page copies of the two latest blocks
   // stay in flight, so the chunk has landed by the first barrier of block
   // 64c - 4 at the latest; slot 64c is first read in the second phase of that
@@ -975,14 +975,13 @@ __global__ __launch_bounds__(512, 1) void attn_dense_pp_kernel(const AttnParams 
 
   const int64_t head_stride = (int64_t)kPage * D;
   const int64_t page_stride = (int64_t)p.hkv * head_stride;
-  // The page copies are issued by the wavefronts of head 1 only (K_PER
-  // copy instructions per page each), in the phase where that head runs its
-  // vector work, so the head issuing products never waits for room in the
-  // vector-memory queue.
-  constexpr int NC = NW * 64;                // copying threads
+  // Each head copies one operand's pages (K_PER copy instructions per page
+  // and wavefront), head 1 the K pages and head 0 the V pages, each in the
+  // phase where that head runs its vector work, so the head issuing products
+  // never waits for room in the vector-memory queue.
+  constexpr int NC = NW * 64;                // copying threads of a head
   constexpr int K_PER = K_TOTAL / NC;
-  const int tidc = tid - NC;                 // valid for the copying threads
-  const int wavec = wave - NW;
+  const int tidc = tid - grp * NC;
   uint32_t coff[K_PER];
 #pragma unroll
   for (int e = 0; e < K_PER; ++e) {
@@ -999,7 +998,7 @@ __global__ __launch_bounds__(512, 1) void attn_dense_pp_kernel(const AttnParams 
 #pragma unroll
     for (int e = 0; e < K_PER; ++e) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(dst + (e * NC + wavec * 64) * 16), 16,
+          rs, (__attribute__((address_space(3))) void*)(dst + (e * NC + wv * 64) * 16), 16,
           (int)coff[e], 0, 0, 0);
     }
   };
@@ -1162,22 +1161,20 @@ __global__ __launch_bounds__(512, 1) void attn_dense_pp_kernel(const AttnParams 
     constexpr int sk = decltype(stage_c)::value;
     constexpr int sv = (sk + NS - 1) % NS;
     constexpr bool kB = decltype(head_c)::value;
-    // ---- phase 2t.  K(t) and V(t - 1) were copied three blocks ago; the
-    // copies of the two blocks since stay in flight.
-    if constexpr (kB) wait_vm_c<2 * 2 * K_PER>();
+    // ---- phase 2t.  K(t) (head 1's copy) and V(t - 1) (head 0's) were
+    // copied three blocks ago; each head's copies of the two blocks since
+    // stay in flight.
+    wait_vm_c<2 * K_PER>();
     lds_barrier();
-    if (kB && wavec == 0 && ((t + 6) & 63) == 0 && t + 6 >= 128 && t + 6 < cnt) {
+    if (kB && wv == 0 && ((t + 6) & 63) == 0 && t + 6 >= 128 && t + 6 < cnt) {
       const int c = (t + 6) >> 6;
       const int x = min(c * 64 + lane, cnt - 1);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(pt + x),
                                        (__attribute__((address_space(3))) void*)&sSlotP[c & 1][0],
                                        4, 0, 0);
     }
-    // K(t + 3) into the stage of K(t - 1), V(t + 2) into that of V(t - 2)
-    if constexpr (kB) {
-      copy_page(p.k_pool, nk, kbuf((sk + NS - 1) % NS));
-      copy_page(p.v_pool, nv, vbuf((sk + 2) % NS));
-    }
+    // K(t + 3) into the stage of K(t - 1)
+    if constexpr (kB) copy_page(p.k_pool, nk, kbuf((sk + NS - 1) % NS));
     const bool pv_on = t > 0 && active(t - 1);
     const bool qk_on = active(t);
     // the head issuing products takes issue priority over the other
@@ -1194,6 +1191,8 @@ __global__ __launch_bounds__(512, 1) void attn_dense_pp_kernel(const AttnParams 
     const int rk = slot_page(min(t + NS, cnt - 1));
     const int rv = slot_page(min(t + NS - 1, cnt - 1));
     if constexpr (!kB) {
+      // V(t + 2) into the stage of V(t - 2), read last in phase 2t - 1
+      copy_page(p.v_pool, nv, vbuf((sk + 2) % NS));
       if (qk_on) vphase(t, sacc, pb);
     } else {
       __builtin_amdgcn_s_setprio(1);
