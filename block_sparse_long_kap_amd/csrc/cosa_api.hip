@@ -433,11 +433,11 @@ COSA_EXPORT cosa_status cosa_sparse_prefill(
   if (e != hipSuccess) return hip_status(e);
   // (sequence, KV head) groups in at most 8 chunks: the proxy of chunk c+1
   // runs while the kernel of chunk c does.  Each chunk's kernel spans at
-  // least kChunkWorkgroups workgroups (eight rounds of two per CU), or the
+  // least kChunkWorkgroups workgroups (sixteen rounds of two per CU), or the
   // launch gaps, the stream hand-offs and the tail of every launch cost more
   // than the hidden proxy time wins: shorter inputs take fewer, larger
   // chunks, down to one on the caller's stream.
-  constexpr int64_t kChunkWorkgroups = 4096;
+  constexpr int64_t kChunkWorkgroups = 8192;
   const int n_groups = p->batch * p->num_kv_heads;
   const int64_t wg_per_group = (int64_t)(p->num_q_heads / p->num_kv_heads) * a.nqb;
   int chunk = (n_groups + 7) / 8;

@@ -297,7 +297,7 @@ cosa_status cosa_osk_prefill(const cosa_problem* p, const void* q, const void* k
  * there.
  *
  * The work is cut into at most 8 chunks of (sequence, KV head) groups, each
- * chunk's kernel at least 4096 workgroups (query heads x query tiles) where
+ * chunk's kernel at least 8192 workgroups (query heads x query tiles) where
  * the groups allow, so short inputs run as one chunk; the proxy of every
  * chunk runs on `stream`.  With aux_stream != NULL (another stream of the
  * same device, not `stream`) and more than one chunk, the kernel of chunk c
