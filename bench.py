@@ -598,6 +598,7 @@ def length_sweep(args, w, bk, torch, dev, stream, ev, budget, tau, headline):
         vis, skp = int(st[:, 0].sum()), int(st[:, 1].sum())
         causal = wn.num_q_heads * sum((min((i + 1) * wn.q_block, n) - 1) // wn.block + 1
                                       for i in range(-(-n // wn.q_block)))
+        fps = flops_per_slot(wn.q_block, wn.head_dim, wn.block)
 
         def fused():
             bk.sparse_prefill(prob, q, kp, vp, budget, tau, aux_stream=side, workspace=ws,
@@ -632,6 +633,10 @@ def length_sweep(args, w, bk, torch, dev, stream, ev, budget, tau, headline):
                           "osk_ms": round(om, 4), "dense_ms": round(dm, 4),
                           "speedup_vs_dense": round(dm / sm, 3),
                           "kap_share": round(km / (km + om), 4),
+                          "osk_mfma_frac": round(fps * (2 * vis - skp) / om / 1e9 /
+                                                 PEAK_BF16_TFLOPS, 4),
+                          "dense_mfma_frac": round(2 * fps * causal / dm / 1e9 /
+                                                   PEAK_BF16_TFLOPS, 4),
                           "stage1_budget": round(vis / causal, 5),
                           "skip_ratio": round(skp / max(vis, 1), 5)}), flush=True)
         del mask, res, dout, ws
