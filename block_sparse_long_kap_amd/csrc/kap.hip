@@ -14,8 +14,8 @@
 // each proxy row.
 //
 // Two launches:
-//   kap_pool_keys  one workgroup per (sequence, key block): streams the page
-//                  of every KV head once from HBM and writes the fp32 mean key
+//   kap_pool_keys  one workgroup per (sequence, key block, KV head): streams
+//                  the head's page once from HBM and writes the fp32 mean key
 //                  split into bf16 hi + lo halves (x ~= hi + lo to 16 bits).
 //   kap_select     one workgroup per (sequence, query head, 4 consecutive
 //                  tiles): pools the tiles' queries from HBM (4 x 8 proxy rows
@@ -77,7 +77,10 @@ __global__ __launch_bounds__(256) void kap_pool_keys(const KapParams p) {
   constexpr int RG = NT / KCH;        // row groups
   __shared__ float red[RG][D];
 
-  const int j = blockIdx.x;   // logical key block (p.ppb pages of kPage keys)
+  // consecutive workgroups take the KV heads of one logical key block (p.ppb
+  // pages of kPage keys), whose slices lie side by side in each page
+  const int j = blockIdx.x / p.hkv;
+  const int g = blockIdx.x - j * p.hkv;
   const int b = blockIdx.y;
   const int q0 = p.cu_seqlens[b];
   const int L = p.cu_seqlens[b + 1] - q0;
@@ -91,34 +94,31 @@ __global__ __launch_bounds__(256) void kap_pool_keys(const KapParams p) {
   const int64_t slab = kbar_slab(p.n_max, D);
   const int64_t plane = (int64_t)p.batch * p.hkv * slab;
 
-  for (int g = 0; g < p.hkv; ++g) {
-    float acc[8];
+  float acc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int r = rg; r < nvalid; r += RG) {
-      const int page = pt[r / kPage];
-      const uint16_t* base = p.k_pool + ((int64_t)page * p.hkv + g) * (kPage * D) + c * 8;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(base + (r % kPage) * D);
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int r = rg; r < nvalid; r += RG) {
+    const int page = pt[r / kPage];
+    const uint16_t* base = p.k_pool + ((int64_t)page * p.hkv + g) * (kPage * D) + c * 8;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(base + (r % kPage) * D);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        acc[2 * w] += bf16_lo(v[w]);
-        acc[2 * w + 1] += bf16_hi(v[w]);
-      }
+    for (int w = 0; w < 4; ++w) {
+      acc[2 * w] += bf16_lo(v[w]);
+      acc[2 * w + 1] += bf16_hi(v[w]);
     }
+  }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[rg][c * 8 + e] = acc[e];
-    __syncthreads();
-    if (tid < D) {
-      float sum = 0.f;
+  for (int e = 0; e < 8; ++e) red[rg][c * 8 + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    float sum = 0.f;
 #pragma unroll
-      for (int k = 0; k < RG; ++k) sum += red[k][tid];
-      uint16_t hi, lo;
-      split_bf16(sum * inv, hi, lo);
-      const int64_t at = ((int64_t)b * p.hkv + g) * slab + kbar_offset<D>(j, tid);
-      p.kbar[at] = hi;
-      p.kbar[plane + at] = lo;
-    }
-    __syncthreads();
+    for (int k = 0; k < RG; ++k) sum += red[k][tid];
+    uint16_t hi, lo;
+    split_bf16(sum * inv, hi, lo);
+    const int64_t at = ((int64_t)b * p.hkv + g) * slab + kbar_offset<D>(j, tid);
+    p.kbar[at] = hi;
+    p.kbar[plane + at] = lo;
   }
 }
 
@@ -1064,7 +1064,8 @@ hipError_t launch_kap_t(const KapParams& p, hipStream_t stream, KapStage stage) 
   const int nkb = p.n_max;
   if (p.batch <= 0 || nkb <= 0) return hipSuccess;
   if (stage & kKapPool) {
-    hipLaunchKernelGGL((kap_pool_keys<D>), dim3(nkb, p.batch), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((kap_pool_keys<D>), dim3((unsigned)(nkb * p.hkv), p.batch), dim3(256), 0,
+                       stream, p);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
